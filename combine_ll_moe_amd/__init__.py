@@ -1,0 +1,126 @@
+"""Python binding of libllmoe.so, the MI355X low-latency MoE dispatch + combine.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name (include/ll_moe.h) and raises LLMoEError on a non-zero status.
+Device buffers may be passed as torch tensors (their data_ptr is used) or as
+raw integer addresses; `stream` defaults to torch's current stream.
+There is no fallback: without the built library this package does not
+import.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libllmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python combine_ll_moe_amd/build.py` "
+        "(hipcc, gfx950) before importing combine_ll_moe_amd")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+BF16 = 0
+FP8_E4M3 = 1
+MAX_TOPK = 16
+MAX_MESSAGE_BYTES = 61440
+
+SUCCESS = 0
+HIP_ERROR = 1
+INTERNAL_ERROR = 3
+INVALID_ARGUMENT = 4
+INVALID_USAGE = 5
+
+_i = ctypes.c_int
+_vp = ctypes.c_void_p
+_szp = ctypes.POINTER(ctypes.c_size_t)
+
+_lib.ll_moe_layout_bytes.argtypes = [_i, _i, _i, _i, _szp]
+_lib.ll_moe_layout_offsets.argtypes = [_i, _i, _i, _i, _i, _szp, _szp, _szp, _szp]
+_lib.ll_moe_dispatch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+_lib.ll_moe_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
+_lib.ll_moe_clean_signals.argtypes = [_vp, _i, _i, _i, _i, _i, _vp]
+_lib.ll_moe_diag_e4m3.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+_lib.ll_moe_status_string.argtypes = [_i]
+_lib.ll_moe_status_string.restype = ctypes.c_char_p
+for _f in ("ll_moe_layout_bytes", "ll_moe_layout_offsets", "ll_moe_dispatch",
+           "ll_moe_combine", "ll_moe_clean_signals", "ll_moe_diag_e4m3"):
+    getattr(_lib, _f).restype = _i
+
+
+class LLMoEError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        name = _lib.ll_moe_status_string(status).decode()
+        super().__init__(f"{call} returned {name} ({status})")
+
+
+def _check(status: int, call: str) -> None:
+    if status != SUCCESS:
+        raise LLMoEError(status, call)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def ll_moe_layout_bytes(max_tokens: int, hidden: int, num_experts: int, dtype: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.ll_moe_layout_bytes(max_tokens, hidden, num_experts, dtype, ctypes.byref(out)),
+           "ll_moe_layout_bytes")
+    return out.value
+
+
+def ll_moe_layout_offsets(max_tokens: int, hidden: int, num_experts: int, dtype: int,
+                          parity: int) -> dict:
+    s, r, g, m = (ctypes.c_size_t() for _ in range(4))
+    _check(_lib.ll_moe_layout_offsets(max_tokens, hidden, num_experts, dtype, parity,
+                                      ctypes.byref(s), ctypes.byref(r), ctypes.byref(g),
+                                      ctypes.byref(m)), "ll_moe_layout_offsets")
+    return {"send": s.value, "recv": r.value, "sig": g.value, "msg_bytes": m.value}
+
+
+def ll_moe_dispatch(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
+                    topk: int, dtype: int, parity: int, x, topk_idx, stream=None) -> None:
+    _check(_lib.ll_moe_dispatch(_ptr(layout), max_tokens, num_tokens, hidden, num_experts, topk,
+                                dtype, parity, _ptr(x), _ptr(topk_idx), _stream(stream)),
+           "ll_moe_dispatch")
+
+
+def ll_moe_combine(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
+                   topk: int, dtype: int, parity: int, expert_out, topk_idx, topk_weights, out,
+                   stream=None) -> None:
+    _check(_lib.ll_moe_combine(_ptr(layout), max_tokens, num_tokens, hidden, num_experts, topk,
+                               dtype, parity, _ptr(expert_out), _ptr(topk_idx),
+                               _ptr(topk_weights), _ptr(out), _stream(stream)),
+           "ll_moe_combine")
+
+
+def ll_moe_clean_signals(layout, max_tokens: int, hidden: int, num_experts: int, dtype: int,
+                         parity: int, stream=None) -> None:
+    _check(_lib.ll_moe_clean_signals(_ptr(layout), max_tokens, hidden, num_experts, dtype, parity,
+                                     _stream(stream)), "ll_moe_clean_signals")
+
+
+def ll_moe_diag_e4m3(inp, out, n: int, stream=None) -> None:
+    """Diagnostic: the fp8 dispatch's e4m3 encoder applied to n fp32 values."""
+    _check(_lib.ll_moe_diag_e4m3(_ptr(inp), _ptr(out), n, _stream(stream)), "ll_moe_diag_e4m3")
+
+
+def raw_status(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes-compatible arguments and return
+    its status without raising (for argument-checking tests)."""
+    return getattr(_lib, name)(*args)

@@ -1,0 +1,157 @@
+// C ABI of libllmoe.so (declared in include/ll_moe.h): argument checks,
+// layout offsets, launch shape, and the launch on the caller's stream.
+// Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ll_moe.h"
+#include "ll_moe_diag.h"
+#include "kernels.h"
+#include "layout.h"
+
+using namespace llmoe;
+
+namespace {
+
+// Workgroups per token for dispatch: enough tokens x groups to give every
+// CU of the 256 about two workgroups, never more groups than messages.
+constexpr int kTargetDispatchBlocks = 512;
+constexpr int kCombineThreads = 256;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_shape(int max_tokens, int num_tokens, int hidden, int num_experts, int topk,
+                int dtype, int parity, Layout* L) {
+  if (parity != 0 && parity != 1) return LL_MOE_INVALID_ARGUMENT;
+  if (!make_layout(max_tokens, hidden, num_experts, dtype, L)) return LL_MOE_INVALID_ARGUMENT;
+  if (num_tokens < 0 || num_tokens > max_tokens) return LL_MOE_INVALID_ARGUMENT;
+  if (topk < 1 || topk > num_experts || topk > LL_MOE_MAX_TOPK) return LL_MOE_INVALID_ARGUMENT;
+  if (dtype == kBf16 && hidden % 8 != 0) return LL_MOE_INVALID_ARGUMENT;
+  if (L->dispatch_msg > kMaxMessageBytes) return LL_MOE_INVALID_ARGUMENT;
+  // slot rows and token offsets are formed in 64 bits, counts in 32
+  if ((int64_t)num_tokens * topk > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
+  return LL_MOE_SUCCESS;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? LL_MOE_SUCCESS : LL_MOE_HIP_ERROR; }
+
+}  // namespace
+
+extern "C" int ll_moe_layout_bytes(int max_tokens, int hidden, int num_experts, int dtype,
+                                   size_t* out_bytes) {
+  Layout L;
+  if (!out_bytes || !make_layout(max_tokens, hidden, num_experts, dtype, &L))
+    return LL_MOE_INVALID_ARGUMENT;
+  *out_bytes = (size_t)L.total;
+  return LL_MOE_SUCCESS;
+}
+
+extern "C" int ll_moe_layout_offsets(int max_tokens, int hidden, int num_experts, int dtype,
+                                     int parity, size_t* send_off, size_t* recv_off,
+                                     size_t* sig_off, size_t* msg_bytes) {
+  Layout L;
+  if (!send_off || !recv_off || !sig_off || (parity != 0 && parity != 1) ||
+      !make_layout(max_tokens, hidden, num_experts, dtype, &L))
+    return LL_MOE_INVALID_ARGUMENT;
+  *send_off = (size_t)L.send_off(parity);
+  *recv_off = (size_t)L.recv_off(parity);
+  *sig_off = (size_t)L.sig_off(parity);
+  if (msg_bytes) *msg_bytes = (size_t)L.dispatch_msg;
+  return LL_MOE_SUCCESS;
+}
+
+extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int hidden,
+                               int num_experts, int topk, int dtype, int parity, const void* x,
+                               const int32_t* topk_idx, hipStream_t stream) {
+  Layout L;
+  int rc = check_shape(max_tokens, num_tokens, hidden, num_experts, topk, dtype, parity, &L);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
+  if (num_tokens > 0 && (!x || !topk_idx || !aligned(x, 16) || !aligned(topk_idx, 4)))
+    return LL_MOE_INVALID_ARGUMENT;
+
+  uint8_t* base = static_cast<uint8_t*>(layout);
+  DispatchParams p;
+  p.send = base + L.send_off(parity);
+  p.recv = base + L.recv_off(parity);
+  p.sig = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity));
+  p.sig_other = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity ^ 1));
+  p.x = static_cast<const uint4*>(x);
+  p.idx = topk_idx;
+  p.num_tokens = num_tokens;
+  p.max_tokens = max_tokens;
+  p.hidden = hidden;
+  p.num_experts = num_experts;
+  p.topk = topk;
+  int groups = num_tokens > 0 ? (kTargetDispatchBlocks + num_tokens - 1) / num_tokens : 1;
+  if (groups > topk + 1) groups = topk + 1;
+  if (groups < 1) groups = 1;
+  p.groups = groups;
+  p.msg_bytes = (uint32_t)L.dispatch_msg;
+  return from_hip(launch_dispatch(p, dtype, stream));
+}
+
+extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int hidden,
+                              int num_experts, int topk, int dtype, int parity,
+                              const void* expert_out, const int32_t* topk_idx,
+                              const float* topk_weights, float* out, hipStream_t stream) {
+  Layout L;
+  int rc = check_shape(max_tokens, num_tokens, hidden, num_experts, topk, dtype, parity, &L);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  if (hidden % 8 != 0) return LL_MOE_INVALID_ARGUMENT;
+  if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
+  if (num_tokens > 0) {
+    if (!expert_out || !topk_idx || !topk_weights || !out) return LL_MOE_INVALID_ARGUMENT;
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(topk_idx, 4) ||
+        !aligned(topk_weights, 4))
+      return LL_MOE_INVALID_ARGUMENT;
+    // out may not overlap the expert outputs
+    const uintptr_t y0 = (uintptr_t)expert_out;
+    const uintptr_t y1 = y0 + (uint64_t)num_experts * max_tokens * hidden * 2;
+    const uintptr_t o0 = (uintptr_t)out;
+    const uintptr_t o1 = o0 + (uint64_t)num_tokens * hidden * 4;
+    if (o0 < y1 && y0 < o1) return LL_MOE_INVALID_ARGUMENT;
+  }
+
+  uint8_t* base = static_cast<uint8_t*>(layout);
+  CombineParams p;
+  p.sig_other = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity ^ 1));
+  p.y = static_cast<const uint4*>(expert_out);
+  p.idx = topk_idx;
+  p.w = topk_weights;
+  p.out = reinterpret_cast<float4*>(out);
+  p.num_tokens = num_tokens;
+  p.max_tokens = max_tokens;
+  p.hidden = hidden;
+  p.num_experts = num_experts;
+  p.topk = topk;
+  p.slices = (hidden / 8 + kCombineThreads - 1) / kCombineThreads;
+  return from_hip(launch_combine(p, stream));
+}
+
+extern "C" int ll_moe_clean_signals(void* layout, int max_tokens, int hidden, int num_experts,
+                                    int dtype, int parity, hipStream_t stream) {
+  Layout L;
+  if (parity != 0 && parity != 1) return LL_MOE_INVALID_ARGUMENT;
+  if (!make_layout(max_tokens, hidden, num_experts, dtype, &L)) return LL_MOE_INVALID_ARGUMENT;
+  if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
+  auto* sig = reinterpret_cast<unsigned long long*>(static_cast<uint8_t*>(layout) + L.sig_off(parity));
+  return from_hip(launch_clean(sig, num_experts, stream));
+}
+
+extern "C" int ll_moe_diag_e4m3(const float* in, uint8_t* out, size_t n, hipStream_t stream) {
+  if (n == 0) return LL_MOE_SUCCESS;
+  if (!in || !out || !aligned(in, 4)) return LL_MOE_INVALID_ARGUMENT;
+  return from_hip(launch_e4m3_probe(in, out, (uint64_t)n, stream));
+}
+
+extern "C" const char* ll_moe_status_string(int status) {
+  switch (status) {
+    case LL_MOE_SUCCESS: return "LL_MOE_SUCCESS";
+    case LL_MOE_HIP_ERROR: return "LL_MOE_HIP_ERROR";
+    case LL_MOE_INTERNAL_ERROR: return "LL_MOE_INTERNAL_ERROR";
+    case LL_MOE_INVALID_ARGUMENT: return "LL_MOE_INVALID_ARGUMENT";
+    case LL_MOE_INVALID_USAGE: return "LL_MOE_INVALID_USAGE";
+    default: return "LL_MOE_UNKNOWN_STATUS";
+  }
+}

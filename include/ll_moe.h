@@ -1,0 +1,175 @@
+/*
+ * ll_moe.h — C ABI of the low-latency MoE dispatch + combine step on one
+ * MI355X (gfx950). Library: libllmoe.so.
+ *
+ * The step, as the pages describe it:
+ *   - rocSHMEM example "LL_MoE/LL_MoE_Buffers.hpp": all buffers are
+ *     allocated once, sized for the worst-case decode micro-batch (file
+ *     comment "Buffer sizing and allocation (DeepEP LL mode style)"); two
+ *     buffer sets for double buffering (struct LLMoEBufferLayout); per set a
+ *     send buffer [num_tokens, hidden+1], a receive buffer
+ *     [num_experts * num_tokens, hidden+1] and one int64 signal word per
+ *     expert (struct LLMoEBuffer); a message is an int followed by hidden
+ *     payload elements (constructor, "Message sizes").
+ *   - mscclpp "mscclpp.h", comment above struct mscclppDevConn: data is put
+ *     first and signalled after; a receiver reads only after it has seen the
+ *     signal.
+ * Dispatch packs every token's top-k copies into per-expert receive slots
+ * and publishes per-expert counts; combine gathers the expert outputs back
+ * to their tokens as a top-k weighted sum in fp32.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers (hipMalloc or equivalent) unless stated.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronizes: a call validates its arguments, enqueues one kernel on
+ *     `stream` and returns. Buffers must stay alive until the stream has
+ *     run the work. Calls may be captured into a HIP graph.
+ *   - Return value: an ll_moe_status_t. Argument errors are found before
+ *     anything is enqueued and leave every buffer untouched. Errors in the
+ *     data (expert ids) are not errors: see "routing" below.
+ *   - Workloads: max_tokens >= 1, 0 <= num_tokens <= max_tokens,
+ *     1 <= topk <= min(num_experts, LL_MOE_MAX_TOPK); bf16 needs
+ *     hidden % 8 == 0, fp8 needs hidden % 128 == 0; a dispatch message may
+ *     not exceed LL_MOE_MAX_MESSAGE_BYTES.
+ *
+ * Routing (topk_idx, int32 [num_tokens, topk], row-major):
+ *   Entry (t, k) names the expert of token t's k-th pick. Expert e owns the
+ *   receive rows [e * max_tokens, (e + 1) * max_tokens) of a set. Slots are
+ *   handed out in ascending token order, and in ascending k within a token:
+ *   slot(t, k) is the number of earlier entries (in (t, k) order) naming the
+ *   same expert. An entry outside [0, num_experts) is masked (no message, no
+ *   count, no combine term); so is an entry whose slot would reach
+ *   max_tokens, which only a token naming one expert twice can cause.
+ *
+ * Parity schedule: every launch with parity q zeroes the signal words of
+ * set 1-q (the clean of the next-parity buffer, struct LLMoEBuffer's
+ * clean_meta() in the rocSHMEM example); dispatch(q) adds its counts to the
+ * signal words of set q, which must be zero when it starts. Step s of a
+ * decode loop runs dispatch(s & 1) then combine(s & 1). After allocating a
+ * layout, clean both sets once (ll_moe_clean_signals with q = 0 and 1).
+ */
+#ifndef LL_MOE_H_
+#define LL_MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Payload type of a dispatch message. */
+typedef enum {
+  LL_MOE_BF16 = 0,      /* hidden bf16 values, unchanged bits */
+  LL_MOE_FP8_E4M3 = 1   /* hidden OCP e4m3 codes + hidden/128 fp32 scales */
+} ll_moe_dtype_t;
+
+/* Status codes; the numbering follows mscclpp.h's mscclppResult_t. */
+typedef enum {
+  LL_MOE_SUCCESS = 0,
+  LL_MOE_HIP_ERROR = 1,         /* the HIP runtime refused the launch */
+  LL_MOE_INTERNAL_ERROR = 3,
+  LL_MOE_INVALID_ARGUMENT = 4,  /* see the conventions above */
+  LL_MOE_INVALID_USAGE = 5
+} ll_moe_status_t;
+
+#define LL_MOE_MAX_TOPK 16
+#define LL_MOE_MAX_MESSAGE_BYTES 61440
+
+/*
+ * ll_moe_layout_bytes — bytes of one layout (both buffer sets).
+ * rocSHMEM example LL_MoE_Buffers.hpp, LLMoEBufferLayout constructor and
+ * get_rdma_size_hint(): with md = dispatch message bytes and mc = combine
+ * message bytes,
+ *   send = max(max_tokens * md, num_experts * max_tokens * mc)
+ *   recv = max(num_experts * max_tokens * md, num_experts * max_tokens * mc)
+ *   total = 2 * send + 2 * recv + 2 * (8 * num_experts).
+ * md = 4 + 2 * hidden (bf16) or 4 + hidden + 4 * (hidden / 128) (fp8: the
+ * e4m3 codes, then one fp32 scale per 128 codes); mc = 4 + 2 * hidden
+ * always (the combine carries bf16). The result is the same for both
+ * dtypes. Host only; enqueues nothing.
+ *   out_bytes (host pointer): receives the total.
+ * Errors: INVALID_ARGUMENT for sizes out of range, a send or receive size
+ * that is not a multiple of 4 (the constructor's ASSERTs), or overflow.
+ */
+int ll_moe_layout_bytes(int max_tokens, int hidden, int num_experts, int dtype,
+                        size_t* out_bytes);
+
+/*
+ * ll_moe_layout_offsets — byte offsets of set `parity` inside a layout:
+ * the pointer table of the LLMoEBufferLayout constructor ("Assign
+ * pointers"): send at parity * send, receive at 2 * send + parity * recv,
+ * signal words at 2 * send + 2 * recv + parity * 8 * num_experts. Within a
+ * set the combine buffers alias the dispatch buffers. Host only.
+ *   send_off, recv_off, sig_off (host pointers): receive the offsets.
+ *   msg_bytes (host pointer, may be NULL): receives md.
+ */
+int ll_moe_layout_offsets(int max_tokens, int hidden, int num_experts, int dtype,
+                          int parity, size_t* send_off, size_t* recv_off,
+                          size_t* sig_off, size_t* msg_bytes);
+
+/*
+ * ll_moe_dispatch — pack every token's messages into set `parity`.
+ *   layout:   device, ll_moe_layout_bytes bytes, 16-byte aligned.
+ *   x:        device, bf16 [num_tokens, hidden] row-major, 16-byte aligned.
+ *   topk_idx: device, int32 [num_tokens, topk], 4-byte aligned.
+ * Writes, for set q = parity:
+ *   send row t (t < num_tokens), at send_q + t * md: message(t);
+ *   receive row e * max_tokens + slot(t, k), at recv_q + row * md, for every
+ *     routed (t, k): message(t);
+ *   signal word e of set q: increased by the number of messages expert e
+ *     received, published with device-scope release semantics after those
+ *     messages (a reader that acquires the word sees them);
+ *   signal words of set 1-q: zeroed.
+ * message(t) = int32 t (little-endian), then for bf16 the bits of x[t],
+ * for fp8 per 128-element block: amax = largest |x| (NaN ignored),
+ * codes e4m3(x * (448 / amax)) rounded to nearest even and saturated to
+ * +-448 (NaN -> 0x7F), then the hidden/128 scales amax / 448 as fp32
+ * (amax = 0 gives scale 0 and zero codes).
+ * No other byte of the layout is written. Enqueued on `stream`.
+ */
+int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int hidden,
+                    int num_experts, int topk, int dtype, int parity,
+                    const void* x, const int32_t* topk_idx, hipStream_t stream);
+
+/*
+ * ll_moe_combine — top-k weighted sum of the expert outputs per token.
+ *   layout:       device, as for dispatch (only the signal words of set
+ *                 1-parity are written: zeroed).
+ *   expert_out:   device, bf16 [num_experts * max_tokens, hidden], 16-byte
+ *                 aligned, in receive-slot order: row e * max_tokens + j is
+ *                 expert e's output for the j-th message it received.
+ *                 Only rows of routed (t, k) are read.
+ *   topk_idx:     device, int32 [num_tokens, topk] (the dispatch routing).
+ *   topk_weights: device, fp32 [num_tokens, topk].
+ *   out:          device, fp32 [num_tokens, hidden], 16-byte aligned; may
+ *                 not overlap expert_out.
+ * out[t, c] = fma chain over k = 0..topk-1 (routed entries only) of
+ *   acc = fmaf(w[t, k], expert_out[e * max_tokens + slot(t, k), c], acc),
+ * starting from +0.0f, in fp32, in ascending k (one fixed order, so that the
+ * result is the same bits on every call). Enqueued on `stream`.
+ */
+int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int hidden,
+                   int num_experts, int topk, int dtype, int parity,
+                   const void* expert_out, const int32_t* topk_idx,
+                   const float* topk_weights, float* out, hipStream_t stream);
+
+/*
+ * ll_moe_clean_signals — zero the num_experts int64 signal words of set
+ * `parity` (the rocSHMEM example's clean_meta(): the dispatch count words
+ * and the combine flag words are one array). Enqueued on `stream`.
+ */
+int ll_moe_clean_signals(void* layout, int max_tokens, int hidden,
+                         int num_experts, int dtype, int parity,
+                         hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* ll_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LL_MOE_H_ */

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, computes the layout the oracle computes, and rejects bad arguments
+before it enqueues anything."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(ll_moe_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported():
+    import combine_ll_moe_amd as ll
+    lib = ctypes.CDLL(ll.LIB_PATH)
+    names = _declared_symbols()
+    assert {"ll_moe_layout_bytes", "ll_moe_dispatch", "ll_moe_combine",
+            "ll_moe_clean_signals"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+SHAPES = [(128, 1024, 8, 0), (128, 7168, 256, 0), (128, 7168, 256, 1), (512, 4096, 64, 0),
+          (1024, 7168, 256, 0), (1, 8, 1, 0), (3, 128, 5, 1), (77, 7168, 256, 1),
+          (33, 1000, 17, 0), (4096, 8192, 512, 1)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_layout_matches_oracle(shape):
+    import combine_ll_moe_amd as ll
+    n, h, e, dt = shape
+    L = oracle.layout(n, h, e, dt)
+    assert ll.ll_moe_layout_bytes(n, h, e, dt) == L["total"]
+    md, _ = oracle.message_bytes(h, dt)
+    for q in (0, 1):
+        o = ll.ll_moe_layout_offsets(n, h, e, dt, q)
+        assert (o["send"], o["recv"], o["sig"], o["msg_bytes"]) == \
+            (L["send"][q], L["recv"][q], L["sig"][q], md)
+
+
+def test_layout_rejections():
+    import combine_ll_moe_amd as ll
+    for args in [(0, 8, 1, 0), (1, 0, 1, 0), (1, 8, 0, 0), (1, 8, 1, 2), (4, 100, 8, 1),
+                 (1, 1, 1, 0), (2**31 - 1, 2**30, 2**31 - 1, 0)]:
+        with pytest.raises(ll.LLMoEError) as ei:
+            ll.ll_moe_layout_bytes(*args)
+        assert ei.value.status == ll.INVALID_ARGUMENT
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("case", [
+    dict(parity=2), dict(parity=-1), dict(num_tokens=129), dict(num_tokens=-1),
+    dict(topk=0), dict(topk=9, num_experts=8), dict(topk=17, num_experts=64),
+    dict(hidden=1020), dict(dtype=1, hidden=1000), dict(dtype=7), dict(layout=0),
+    dict(layout=FAKE + 8), dict(x=0), dict(x=FAKE + 4), dict(idx=0), dict(idx=FAKE + 2),
+    dict(max_tokens=0), dict(hidden=8 * 4000),
+])
+def test_dispatch_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
+             dtype=0, parity=0, x=FAKE, idx=FAKE)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_dispatch", a["layout"], a["max_tokens"], a["num_tokens"],
+                       a["hidden"], a["num_experts"], a["topk"], a["dtype"], a["parity"],
+                       a["x"], a["idx"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("case", [
+    dict(parity=3), dict(num_tokens=200), dict(topk=0), dict(hidden=1020), dict(y=0),
+    dict(w=0), dict(out=0), dict(out=FAKE + 4), dict(y=FAKE + 8), dict(w=FAKE + 1),
+    dict(out=FAKE + 64),  # overlaps expert_out
+])
+def test_combine_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
+             dtype=0, parity=0, y=FAKE, idx=FAKE, w=FAKE, out=FAKE * 1024)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_combine", a["layout"], a["max_tokens"], a["num_tokens"],
+                       a["hidden"], a["num_experts"], a["topk"], a["dtype"], a["parity"],
+                       a["y"], a["idx"], a["w"], a["out"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
+def test_clean_rejects_bad_arguments():
+    import combine_ll_moe_amd as ll
+    assert ll.raw_status("ll_moe_clean_signals", FAKE, 8, 64, 4, 0, 2, None) == ll.INVALID_ARGUMENT
+    assert ll.raw_status("ll_moe_clean_signals", 0, 8, 64, 4, 0, 0, None) == ll.INVALID_ARGUMENT
+    assert ll.raw_status("ll_moe_clean_signals", FAKE, 0, 64, 4, 0, 0, None) == ll.INVALID_ARGUMENT
+    assert ll.raw_status("ll_moe_diag_e4m3", 0, FAKE, 4, None) == ll.INVALID_ARGUMENT
+
+
+def test_binding_routes_through_the_library_only():
+    """The binding imports neither the oracle nor the workload generators."""
+    src = open(os.path.join(ROOT, "combine_ll_moe_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "import workloads" not in src
+    for f in glob.glob(os.path.join(ROOT, "combine_ll_moe_amd", "csrc", "*")):
+        text = open(f).read()
+        assert "oracle" not in text and "ll_moe_oracle" not in text, f

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs. Dispatch buffers and signal words must match byte for
+byte, with no byte written outside them; combine outputs must be within
+1e-6 relative error of the oracle (and are expected to be bit-identical)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import combine_ll_moe_amd as ll  # noqa: E402
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from _gpu import DEV, Step, check_combine, filled_mask, say, to_dev  # noqa: E402
+
+
+def _inputs(w: W.Workload, dense_y=False):
+    x, idx, wt = W.tokens(w), W.routing(w), W.weights(w)
+    y = W.expert_outputs(w, None if dense_y else filled_mask(w, idx))
+    return x, idx, wt, y
+
+
+def _run_step(st: Step, q, x, idx, wt, y, y_dev=None):
+    st.dispatch(q, x, idx)
+    st.check_dispatch(q, idx)
+    out, ref = st.combine(q, y, idx, wt, y_dev=y_dev)
+    st.check_signals()
+    diff = check_combine(out, ref)
+    assert diff == 0, f"{diff} combine outputs differ in bits"
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode_fp8", "wide_zipf", "worst_fill"])
+def test_workload_both_parities(name):
+    w = W.WORKLOADS[name]
+    say(f"[parity] {name}: N={w.num_tokens} h={w.hidden} E={w.num_experts} K={w.topk} "
+        f"dtype={w.dtype}")
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=(name == "tiny"))
+    y_dev = to_dev(y)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y, y_dev)
+        say(f"[parity] {name} parity {q} ok")
+
+
+def test_hundred_steps_tiny_every_byte():
+    base = W.WORKLOADS["tiny"]
+    st = Step(base, full_image=True)
+    for s in range(100):
+        w = base.with_(seed=1000 + s)
+        x, idx, wt, y = _inputs(w)
+        _run_step(st, s & 1, x, idx, wt, y)
+    say("[seq] tiny 100 steps ok")
+
+
+def test_hundred_steps_decode():
+    base = W.WORKLOADS["decode"]
+    st = Step(base, full_image=False)
+    y = W.expert_outputs(base)          # every row filled: one upload for all steps
+    y_dev = to_dev(y)
+    for s in range(100):
+        w = base.with_(seed=2000 + s)
+        x, idx, wt = W.tokens(w), W.routing(w), W.weights(w)
+        q = s & 1
+        st.dispatch(q, x, idx)
+        st.check_dispatch(q, idx)
+        out, ref = st.combine(q, y, idx, wt, y_dev=y_dev)
+        assert check_combine(out, ref) == 0
+    say("[seq] decode 100 steps ok")
+
+
+@pytest.mark.parametrize("n", [0, 1, 77, 127])
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3])
+def test_ragged_batches(n, dtype):
+    w = W.Workload("ragged", n, 7168, 256, 8, dtype, "uniform", max_tokens=128, seed=n)
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    for q in (1, 0):
+        _run_step(st, q, x, idx, wt, y)
+
+
+@pytest.mark.parametrize("shape", [
+    # (N, Nmax, h, E, K, dtype)
+    (5, 8, 8, 1, 1, W.BF16),        # smallest message: 20 bytes
+    (9, 9, 24, 3, 2, W.BF16),       # odd capacity, short rows
+    (33, 40, 1032, 17, 5, W.BF16),  # ragged chunk counts
+    (16, 16, 512, 64, 16, W.BF16),  # the 16-pick path
+    (16, 16, 512, 64, 9, W.BF16),   # 16-pick path with 9 picks
+    (3, 3, 128, 5, 4, W.FP8_E4M3),  # one fp8 block
+    (64, 64, 384, 32, 3, W.FP8_E4M3),
+    (300, 300, 2048, 128, 8, W.BF16),
+])
+@pytest.mark.parametrize("pad", [0, 16, 48])
+def test_shapes_and_base_phases(shape, pad):
+    n, cap, h, e, k, dt = shape
+    w = W.Workload("shape", n, h, e, k, dt, "uniform", max_tokens=cap, seed=h + k)
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=True, base_pad=pad)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
+def test_masked_repeated_and_overflowing_picks():
+    w = W.Workload("mask", 6, 64, 4, 3, W.BF16, "uniform", max_tokens=6, seed=9)
+    x = W.tokens(w)
+    idx = np.array([[0, -1, 2], [2, 2, 7], [0, 0, 0], [1, 3, 0], [0, 0, 2**31 - 1],
+                    [-2**31, 0, 0]], np.int32)
+    wt = W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+    _, cnt = oracle.route(idx, 4, 6)
+    assert cnt[0] == 6  # capacity reached: later picks of expert 0 dropped
+
+
+def test_fp8_special_blocks():
+    w = W.Workload("fp8s", 8, 1024, 8, 2, W.FP8_E4M3, "uniform", seed=4)
+    x = W.tokens(w)
+    x[0, :128] = 0                                                   # amax 0
+    x[0, 128:256] = 0x8000                                           # all -0
+    x[1, :128] = W.f32_to_bf16_bits(np.full(128, 3e-38, np.float32))  # tiny normal
+    x[1, 128:256] = np.arange(128, dtype=np.uint16)                  # subnormals, amax 2^-126 * ...
+    x[2, :128] = 0x0001                                              # smallest subnormal: inv overflows
+    x[2, 1] = 0
+    x[3, 5] = 0x7F80                                                 # +inf in a block
+    x[3, 200] = 0xFF80                                               # -inf
+    x[4, 7] = 0x7FC0                                                 # quiet NaN
+    x[4, 300] = 0x7F81                                               # signalling NaN pattern
+    x[5, :128] = W.f32_to_bf16_bits(np.linspace(-448, 448, 128).astype(np.float32))
+    x[6, 256:384] = W.f32_to_bf16_bits(np.full(128, 65504.0, np.float32))
+    idx = W.routing(w)
+    wt = W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
+def test_dispatch_accumulates_when_set_not_cleaned():
+    """dispatch(q) adds to set q's words; without a launch of the other
+    parity in between they are not cleaned, on both sides alike."""
+    w = W.WORKLOADS["tiny"]
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    st.dispatch(0, x, idx)
+    st.dispatch(0, x, idx)
+    torch.cuda.synchronize()
+    st.check_signals()
+    g, _ = st.signals(0)
+    assert g.sum() == 2 * idx.size
+
+
+def test_clean_only_touches_its_set():
+    w = W.WORKLOADS["tiny"]
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=True)
+    st.dispatch(1, x, idx)
+    st.clean(0)
+    st.clean(1)
+    st.check_dispatch(1, idx)
+
+
+def test_identity_round_trip_exact():
+    """Experts that return their input and weights 1/8: every partial sum
+    is exact, so combine(dispatch(x)) returns f32(x) exactly (a -0 input
+    returns +0, the chain's starting value)."""
+    w = W.WORKLOADS["decode"]
+    x, idx = W.tokens(w), W.routing(w)
+    st = Step(w, full_image=False)
+    st.dispatch(0, x, idx)
+    st.check_dispatch(0, idx, restore=False)
+    md = st.md
+    r0 = st.L["recv"][0]
+    nrow = w.num_experts * w.capacity
+    recv = st.img[r0:r0 + nrow * md].reshape(nrow, md)
+    y = np.zeros((nrow, w.hidden), np.uint16)
+    mask = filled_mask(w, idx)
+    y[mask] = np.ascontiguousarray(recv[mask][:, 4:]).view(np.uint16)
+    wt = np.full(idx.shape, 1.0 / 8, np.float32)
+    out, ref = st.combine(0, y, idx, wt)
+    xf = W.bf16_bits_to_f32(x)
+    # the chain starts from +0.0f, so an input -0 comes back as +0
+    nz = xf != 0
+    for o in (ref, out):
+        assert np.array_equal(o, xf)
+        assert np.array_equal(o[nz].view(np.uint32), xf[nz].view(np.uint32))
+
+
+def _all_rounding_inputs():
+    top = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = [0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xFEDC]
+    return np.concatenate([top | np.uint32(lo) for lo in lows]).view(np.float32)
+
+
+def test_e4m3_encoder_against_oracle():
+    rng = np.random.default_rng(3)
+    rnd = rng.integers(0, 1 << 32, 1 << 24, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    for v in (_all_rounding_inputs(), rnd):
+        d_in = torch.from_numpy(v.copy()).to(DEV)
+        d_out = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+        ll.ll_moe_diag_e4m3(d_in, d_out, v.size)
+        got = d_out.cpu().numpy()
+        want = oracle.e4m3(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, [(hex(v.view(np.uint32)[i]), got[i], want[i]) for i in bad[:8]]
+
+
+def test_repeated_calls_same_bits():
+    """Fixed operand order: the same inputs give the same bits every call."""
+    w = W.WORKLOADS["wide_zipf"]
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    y_dev = to_dev(y)
+    outs = []
+    for s in range(4):
+        st.dispatch(s & 1, x, idx)
+        o, ref = st.combine(s & 1, y, idx, wt, y_dev=y_dev)
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))

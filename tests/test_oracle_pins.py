@@ -417,10 +417,12 @@ def test_combine_never_reads_unfilled_rows():
 @pytest.mark.parametrize("K", [2, 4, 8])
 def test_identity_round_trip_is_exact(K):
     """Experts that return their input, weights 1/K (a power of two): every
-    partial sum m*x/K is exact in fp32, so combine(dispatch(x)) == x."""
+    partial sum m*x/K is exact in fp32, so combine(dispatch(x)) == x (a -0
+    input returns +0, the chain's starting value)."""
     E, N, h = 9, 30, 96
     w = W.Workload("t", N, h, E, K, W.BF16, "uniform", seed=K)
     x, idx = W.tokens(w), W.routing(w)
+    x[0, :3] = [0x8000, 0x0000, 0x0001]  # -0, +0, the smallest subnormal
     img = oracle.new_image(N, h, E, W.BF16, fill=0)
     oracle.dispatch(img, N, h, E, W.BF16, 0, x, idx)
     md, _ = oracle.message_bytes(h, W.BF16)
@@ -429,7 +431,13 @@ def test_identity_round_trip_is_exact(K):
     y = np.ascontiguousarray(recv[:, 4:]).view(np.uint16)   # expert = identity
     wt = np.full((N, K), 1.0 / K, np.float32)
     out = oracle.combine(img, N, h, E, W.BF16, 0, y, idx, wt)
-    assert np.array_equal(out.view(np.uint32), W.bf16_bits_to_f32(x).view(np.uint32))
+    xf = W.bf16_bits_to_f32(x)
+    # the chain starts from +0.0f: a -0 input returns +0; every other value
+    # returns with its exact bits
+    assert np.array_equal(out, xf)
+    nz = xf != 0
+    assert np.array_equal(out[nz].view(np.uint32), xf[nz].view(np.uint32))
+    assert out[0, 0] == 0 and not np.signbit(out[0, 0])
 
 
 def test_one_hot_weights_gather_exactly():
