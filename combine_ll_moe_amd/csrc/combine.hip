@@ -43,29 +43,45 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   const int c = sl * blockDim.x + tid;
   if (c >= chunks) return;
 
-  uint4 v[MAXK];
-  float wk[MAXK];
+  // Rows of the routed picks; a masked pick borrows the row of a routed
+  // one so that every load is unconditional (the borrowed value is never
+  // used). A token with no routed pick reads nothing.
+  uint64_t row[MAXK];
+  bool routed[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    v[k] = make_uint4(0, 0, 0, 0);
-    wk[k] = 0.0f;
-    if (k < P.topk && rs.slot[k] >= 0) {
-      const uint64_t row = (uint64_t)rs.expert[k] * (uint64_t)P.max_tokens + (uint64_t)rs.slot[k];
-      v[k] = P.y[row * (uint64_t)chunks + c];
-      wk[k] = P.w[(uint64_t)t * P.topk + k];
-    }
+    const int s = rs.slot[k];    // past topk: never read as a slot
+    const int e = rs.expert[k];
+    routed[k] = k < P.topk && s >= 0;
+    row[k] = (uint64_t)(routed[k] ? e : 0) * (uint64_t)P.max_tokens + (uint64_t)(routed[k] ? s : 0);
+  }
+  bool any = false;
+  uint64_t fallback = 0;
+#pragma unroll
+  for (int k = MAXK - 1; k >= 0; --k) {
+    fallback = routed[k] ? row[k] : fallback;
+    any = any || routed[k];
   }
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  if (any) {
+    uint4 v[MAXK];
+    float wk[MAXK];
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    if (k < P.topk && rs.slot[k] >= 0) {
+    for (int k = 0; k < MAXK; ++k) {
+      v[k] = P.y[(routed[k] ? row[k] : fallback) * (uint64_t)chunks + c];
+      wk[k] = P.w[(uint64_t)t * P.topk + (k < P.topk ? k : P.topk - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
       const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = __builtin_fmaf(wk[k], __uint_as_float(q[j] << 16), acc[2 * j]);
-        acc[2 * j + 1] = __builtin_fmaf(wk[k], __uint_as_float(q[j] & 0xFFFF0000u), acc[2 * j + 1]);
+        const float a = __builtin_fmaf(wk[k], __uint_as_float(q[j] << 16), acc[2 * j]);
+        const float b = __builtin_fmaf(wk[k], __uint_as_float(q[j] & 0xFFFF0000u), acc[2 * j + 1]);
+        acc[2 * j] = routed[k] ? a : acc[2 * j];
+        acc[2 * j + 1] = routed[k] ? b : acc[2 * j + 1];
       }
     }
   }
@@ -76,7 +92,11 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int blocks = p.num_tokens > 0 ? p.num_tokens * p.slices : 1;
-  if (p.topk <= 8)
+  if (p.topk <= 2)
+    combine_kernel<2><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 4)
+    combine_kernel<4><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 8)
     combine_kernel<8><<<blocks, kCombineBlock, 0, stream>>>(p);
   else
     combine_kernel<16><<<blocks, kCombineBlock, 0, stream>>>(p);

@@ -1,19 +1,23 @@
 // Device-side routing prologue shared by the dispatch and combine kernels.
 //
 // The receive buffer of a set holds num_experts * max_tokens message rows
-// (rocSHMEM example LL_MoE_Buffers.hpp, struct LLMoEBuffer, dispatch receive
-// buffer); expert e owns rows [e * max_tokens, (e + 1) * max_tokens). A
-// routed entry (t, k) goes to row e * max_tokens + slot(t, k), where
+// (rocSHMEM example LL_MoE/LL_MoE_Buffers.hpp, struct LLMoEBuffer, dispatch
+// receive buffer); expert e owns rows [e * max_tokens, (e + 1) * max_tokens).
+// A routed entry (t, k) goes to row e * max_tokens + slot(t, k), where
 // slot(t, k) counts the earlier entries, in (t, k) order, that name the same
-// expert. That is an exclusive prefix count per expert in ascending token
-// order, which makes the slot order deterministic.
+// expert: the entries of tokens before t, plus the picks of t itself before
+// k. That is an exclusive prefix count per expert in ascending token order,
+// which makes the slot order deterministic.
 //
-// Every workgroup that serves token t recomputes the K slots of t from the
-// routing table itself: it scans the table up to t and counts matches per
-// pick with per-lane counters, then reduces them across the wavefront and
-// the workgroup. The table is at most a few tens of KiB and stays in L2, so
-// the redundant scan costs L2 reads instead of a second launch or a
-// workspace.
+// Every workgroup that serves token t recomputes the slots of t from the
+// routing table itself (no workspace, no second launch): the table is at
+// most a few tens of KiB and stays in L2.
+//  - Up to kHistExperts experts: a per-expert histogram of the earlier
+//    tokens' entries in LDS, one LDS atomic per entry whatever topk is.
+//  - More experts: a ballot per (entry, pick) over the earlier entries,
+//    summed across the wavefronts in LDS.
+// Loads are unconditional (indices clamped into the table, clamped lanes
+// masked afterwards), so the compiler issues them back to back.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,17 +29,19 @@ namespace llmoe {
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;
+constexpr int kHistExperts = 4096;
 
 struct RouteShared {
-  int expert[kMaxTopk];  // idx[t, k]
-  int slot[kMaxTopk];    // slot(t, k), or -1 when the entry is masked
+  alignas(16) int expert[kMaxTopk];  // idx[t, k]
+  alignas(16) int slot[kMaxTopk];    // slot(t, k), or -1 when the entry is masked
   int partial[kMaxWaves][kMaxTopk];
+  int hist[kHistExperts];
 };
 
 // All threads of the workgroup must call this (it contains barriers).
 // On return rs.expert[k] and rs.slot[k] hold token t's picks and slots for
 // k < topk. blockDim.x must be a multiple of 64 and at most 1024, and
-// topk <= MAXK <= kMaxTopk.
+// 1 <= topk <= MAXK <= kMaxTopk.
 template <int MAXK>
 __device__ __forceinline__ void route_token(const int32_t* __restrict__ idx, int t, int topk,
                                             int num_experts, int max_tokens, RouteShared& rs) {
@@ -43,45 +49,78 @@ __device__ __forceinline__ void route_token(const int32_t* __restrict__ idx, int
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int nthreads = blockDim.x;
-  const int64_t first = (int64_t)t * topk;  // entries of earlier tokens: [0, first)
-  const int64_t end = first + topk;
+  const int first = t * topk;  // entries of earlier tokens: [0, first)
+  constexpr int kUnroll = 8;
 
-  if (tid < topk) rs.expert[tid] = idx[first + tid];
-  __syncthreads();
-
+  // the token's own picks (uniform; picks past topk repeat the last one and
+  // are never used)
   int pick[MAXK];
-  int cnt[MAXK];  // wave-uniform
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    pick[k] = k < topk ? rs.expert[k] : INT32_MIN;
-    cnt[k] = 0;
+  for (int k = 0; k < MAXK; ++k) pick[k] = idx[first + (k < topk ? k : topk - 1)];
+
+  if (num_experts <= kHistExperts) {
+    for (int e = tid; e < num_experts; e += nthreads) rs.hist[e] = 0;
+    __syncthreads();
+    const int last = first > 0 ? first - 1 : 0;
+    for (int base = tid; base < first; base += nthreads * kUnroll) {
+      int v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = base + u * nthreads;
+        v[u] = idx[p < last ? p : last];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int p = base + u * nthreads;
+        if (p < first && v[u] >= 0 && v[u] < num_experts) atomicAdd(&rs.hist[v[u]], 1);
+      }
+    }
+    __syncthreads();
+    if (tid < topk) {
+      int e = pick[0];  // this thread's pick, and how often it came earlier in t
+      int same = 0;
+#pragma unroll
+      for (int k = 0; k < MAXK; ++k) e = k == tid ? pick[k] : e;
+#pragma unroll
+      for (int k = 0; k < MAXK; ++k) same += (k < tid) & (pick[k] == e);
+      const bool valid = e >= 0 && e < num_experts;
+      const int s = valid ? rs.hist[e] + same : 0;
+      rs.expert[tid] = e;
+      rs.slot[tid] = valid && s < max_tokens ? s : -1;
+    }
+    __syncthreads();
+    return;
   }
 
-  // Entry p counts for pick k when it names the same expert and comes
-  // before (t, k): p < first + k. Each lane loads eight entries per round
-  // (independent loads, all in flight together); a ballot per (entry, pick)
-  // turns the 64 comparisons of a wavefront into one scalar popcount. The
-  // round count is the same for every lane of the workgroup.
-  constexpr int kUnroll = 8;
-  for (int64_t base = (int64_t)wave * kWave; base < end; base += (int64_t)nthreads * kUnroll) {
+  // many experts: one ballot per (entry, pick); entry p counts for pick k
+  // when it names the same expert and comes before (t, k): p < first + k
+  const int end = first + topk;
+  const int last = end - 1;
+  int cnt[MAXK];  // wave-uniform
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) cnt[k] = 0;
+  for (int base = wave * kWave; base < end; base += nthreads * kUnroll) {
     int v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t p = base + lane + (int64_t)u * nthreads;
-      v[u] = p < end ? idx[p] : INT32_MIN + 1;
+      const int p = base + lane + u * nthreads;
+      v[u] = idx[p < last ? p : last];
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t p = base + lane + (int64_t)u * nthreads;
+      const int p = base + lane + u * nthreads;
 #pragma unroll
-      for (int k = 0; k < MAXK; ++k)
-        if (k < topk) cnt[k] += __popcll(__ballot(v[u] == pick[k] && p < first + k));
+      for (int k = 0; k < MAXK; ++k) cnt[k] += __popcll(__ballot(v[u] == pick[k] && p < first + k));
     }
   }
-
+  if (lane == 0) {
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k)
-    if (k < topk && lane == 0) rs.partial[wave][k] = cnt[k];
+    for (int k = 0; k < MAXK; ++k) rs.partial[wave][k] = cnt[k];
+  }
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) rs.expert[k] = pick[k];
+  }
   __syncthreads();
   if (tid < topk) {
     int s = 0;

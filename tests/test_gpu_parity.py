@@ -91,6 +91,9 @@ def test_ragged_batches(n, dtype):
     (3, 3, 128, 5, 4, W.FP8_E4M3),  # one fp8 block
     (64, 64, 384, 32, 3, W.FP8_E4M3),
     (300, 300, 2048, 128, 8, W.BF16),
+    (40, 40, 64, 4096, 4, W.BF16),   # largest expert count of the LDS histogram
+    (40, 48, 64, 4097, 4, W.BF16),   # ballot path beyond it
+    (24, 24, 256, 5000, 12, W.FP8_E4M3),
 ])
 @pytest.mark.parametrize("pad", [0, 16, 48])
 def test_shapes_and_base_phases(shape, pad):
