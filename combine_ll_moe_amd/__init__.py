@@ -23,7 +23,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 BF16 = 0
 FP8_E4M3 = 1
 MAX_TOPK = 16
-MAX_MESSAGE_BYTES = 61440
+MAX_MESSAGE_BYTES = 45056
+MAX_EXPERTS = 1 << 20
 
 SUCCESS = 0
 HIP_ERROR = 1

@@ -8,15 +8,25 @@
 #include "ll_moe_diag.h"
 #include "kernels.h"
 #include "layout.h"
+#include "route.h"
 
 using namespace llmoe;
 
 namespace {
 
-// Workgroups per token for dispatch: enough tokens x groups to give every
-// CU of the 256 about two workgroups, never more groups than messages.
-constexpr int kTargetDispatchBlocks = 512;
-constexpr int kCombineThreads = 256;
+// Launch shapes. Dispatch: a workgroup takes a tile of consecutive tokens
+// and every groups-th message of each; combine: a tile of tokens and one run
+// of columns. Tiles grow (sharing one routing prologue among more tokens)
+// once there are enough workgroups to give each of the 256 CUs about two.
+constexpr int kTargetBlocks = 512;
+constexpr int kMaxTileTokens = 2;
+
+int tile_for(int num_tokens, int per_token_blocks, int topk) {
+  int tile = (int)(((int64_t)num_tokens * per_token_blocks) / kTargetBlocks);
+  if (tile > kMaxTileTokens) tile = kMaxTileTokens;
+  if (tile > kMaxTileEntries / topk) tile = kMaxTileEntries / topk;
+  return tile < 1 ? 1 : tile;
+}
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -28,8 +38,9 @@ int check_shape(int max_tokens, int num_tokens, int hidden, int num_experts, int
   if (topk < 1 || topk > num_experts || topk > LL_MOE_MAX_TOPK) return LL_MOE_INVALID_ARGUMENT;
   if (dtype == kBf16 && hidden % 8 != 0) return LL_MOE_INVALID_ARGUMENT;
   if (L->dispatch_msg > kMaxMessageBytes) return LL_MOE_INVALID_ARGUMENT;
-  // slot rows and token offsets are formed in 64 bits, counts in 32
-  if ((int64_t)num_tokens * topk > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
+  if (num_experts > LL_MOE_MAX_EXPERTS) return LL_MOE_INVALID_ARGUMENT;
+  // slot rows and token offsets are formed in 64 bits, entry indices in 32
+  if ((int64_t)max_tokens * topk > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
   return LL_MOE_SUCCESS;
 }
 
@@ -83,11 +94,14 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   p.hidden = hidden;
   p.num_experts = num_experts;
   p.topk = topk;
-  int groups = num_tokens > 0 ? (kTargetDispatchBlocks + num_tokens - 1) / num_tokens : 1;
+  int groups = num_tokens > 0 ? (kTargetBlocks + num_tokens - 1) / num_tokens : 1;
   if (groups > topk + 1) groups = topk + 1;
   if (groups < 1) groups = 1;
   p.groups = groups;
+  p.tile = tile_for(num_tokens, groups, topk);
   p.msg_bytes = (uint32_t)L.dispatch_msg;
+  p.msg_stride = ((uint32_t)kMsgLdsOffset + p.msg_bytes + 15u) & ~15u;
+  p.nbuf = 2 * p.msg_stride <= kDispatchLdsBudget ? 2 : 1;
   return from_hip(launch_dispatch(p, dtype, stream));
 }
 
@@ -125,7 +139,8 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   p.hidden = hidden;
   p.num_experts = num_experts;
   p.topk = topk;
-  p.slices = (hidden / 8 + kCombineThreads - 1) / kCombineThreads;
+  p.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
+  p.tile = tile_for(num_tokens, p.slices, topk);
   return from_hip(launch_combine(p, stream));
 }
 

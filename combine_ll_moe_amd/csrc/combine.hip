@@ -10,11 +10,13 @@
 // (struct LLMoEBuffer, combine buffers) becomes a direct gather from the
 // expert outputs, as a one-shot reduction replaces push-then-fold.
 //
-// Design on gfx950: one workgroup per (token, run of columns). It computes
-// the token's slots (route.h), then every thread issues its topk 16-byte
-// loads of bf16 expert rows at once (all outstanding together), folds them
-// with v_fma_f32 in k order, and writes 8 fp32 results as two 16-byte
-// stores. Workgroup 0 zeroes the other set's signal words.
+// Design on gfx950: one workgroup per (tile of consecutive tokens, run of
+// columns). It computes the tile's slots once (route.h); then, token by
+// token, every thread issues its topk 16-byte loads of bf16 expert rows at
+// once (all outstanding together, and the next token's requested before the
+// current one is reduced), folds them with v_fma_f32 in k order, and writes
+// 8 fp32 results as two 16-byte stores. Workgroup 0 zeroes the other set's
+// signal words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,38 +24,29 @@
 #include "layout.h"
 #include "route.h"
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 namespace llmoe {
 
-constexpr int kCombineBlock = 256;
-
+// Gather-reduce of token t (entry row i of the tile) over this thread's 8
+// columns. A masked pick borrows a routed pick's row address so that the
+// loads stay unconditional; its value is never used, and a token with no
+// routed pick reads nothing.
 template <int MAXK>
-__global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombineParams P) {
-  __shared__ RouteShared rs;
-  const int tid = threadIdx.x;
-  if (blockIdx.x == 0)
-    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
-
-  const int t = blockIdx.x / P.slices;
-  const int sl = blockIdx.x - t * P.slices;
-  if (t >= P.num_tokens) return;
-
-  route_token<MAXK>(P.idx, t, P.topk, P.num_experts, P.max_tokens, rs);
-
-  const int chunks = P.hidden / 8;
-  const int c = sl * blockDim.x + tid;
-  if (c >= chunks) return;
-
-  // Rows of the routed picks; a masked pick borrows the row of a routed
-  // one so that every load is unconditional (the borrowed value is never
-  // used). A token with no routed pick reads nothing.
+__device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs, int t,
+                                              int i, int c, int chunks) {
+  const u32x4* y = reinterpret_cast<const u32x4*>(P.y);
   uint64_t row[MAXK];
   bool routed[MAXK];
+  float w[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    const int s = rs.slot[k];    // past topk: never read as a slot
-    const int e = rs.expert[k];
+    const int kk = k < P.topk ? k : 0;
+    const int s = rs.slot[i * P.topk + kk];
     routed[k] = k < P.topk && s >= 0;
-    row[k] = (uint64_t)(routed[k] ? e : 0) * (uint64_t)P.max_tokens + (uint64_t)(routed[k] ? s : 0);
+    row[k] = (uint64_t)(routed[k] ? rs.expert[i * P.topk + kk] : 0) * (uint64_t)P.max_tokens +
+             (uint64_t)(routed[k] ? s : 0);
+    w[k] = P.w[(uint64_t)t * P.topk + kk];
   }
   bool any = false;
   uint64_t fallback = 0;
@@ -66,22 +59,18 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   if (any) {
-    uint4 v[MAXK];
-    float wk[MAXK];
+    u32x4 v[MAXK];
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      v[k] = P.y[(routed[k] ? row[k] : fallback) * (uint64_t)chunks + c];
-      wk[k] = P.w[(uint64_t)t * P.topk + (k < P.topk ? k : P.topk - 1)];
-    }
+    for (int k = 0; k < MAXK; ++k) v[k] = y[(routed[k] ? row[k] : fallback) * (uint64_t)chunks + c];
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
       const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = __builtin_fmaf(wk[k], __uint_as_float(q[j] << 16), acc[2 * j]);
-        const float b = __builtin_fmaf(wk[k], __uint_as_float(q[j] & 0xFFFF0000u), acc[2 * j + 1]);
-        acc[2 * j] = routed[k] ? a : acc[2 * j];
-        acc[2 * j + 1] = routed[k] ? b : acc[2 * j + 1];
+      for (int h = 0; h < 4; ++h) {
+        const float a = __builtin_fmaf(w[k], __uint_as_float(q[h] << 16), acc[2 * h]);
+        const float b = __builtin_fmaf(w[k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
+        acc[2 * h] = routed[k] ? a : acc[2 * h];
+        acc[2 * h + 1] = routed[k] ? b : acc[2 * h + 1];
       }
     }
   }
@@ -90,8 +79,31 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+template <int MAXK>
+__global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombineParams P) {
+  __shared__ RouteShared rs;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
+
+  // workgroup -> (tile of tokens [t0, t1), run of columns sl)
+  const int tile = blockIdx.x / P.slices;
+  const int sl = blockIdx.x - tile * P.slices;
+  const int t0 = tile * P.tile;
+  if (t0 >= P.num_tokens) return;
+  const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
+
+  route_tile(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs);
+
+  const int chunks = P.hidden / 8;
+  const int c = sl * blockDim.x + tid;
+  if (c >= chunks) return;
+  for (int t = t0; t < t1; ++t) combine_token<MAXK>(P, rs, t, t - t0, c, chunks);
+}
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const int blocks = p.num_tokens > 0 ? p.num_tokens * p.slices : 1;
+  const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
+  const int blocks = tiles * p.slices;
   if (p.topk <= 2)
     combine_kernel<2><<<blocks, kCombineBlock, 0, stream>>>(p);
   else if (p.topk <= 4)

@@ -35,10 +35,6 @@
 
 namespace llmoe {
 
-constexpr int kDispatchBlock = 256;
-// The message sits at this LDS byte offset, so that its payload (message
-// byte 4) starts 16-byte aligned and the row of x lands with ds_write_b128.
-constexpr int kMsgLdsOffset = 12;
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -64,21 +60,28 @@ __device__ __forceinline__ void store_b32(uint32_t v, BufRsrc r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCachePolicySc1);
 }
 
-// fp32 -> OCP e4m3 ("e4m3fn") code, round to nearest even, saturating to
-// +-448; the infinities saturate and every NaN gives 0x7F. Integer form:
-// normal codes round the fp32 mantissa at bit 20 and rebias the exponent
-// (127 -> 7); below 2^-6 the code counts 2^-9 steps, taken with rint.
-__device__ __forceinline__ uint32_t e4m3_code(float p) {
-  const uint32_t u = __float_as_uint(p);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const float sub_steps = __uint_as_float(a < 0x3C800000u ? a : 0x3C800000u) * 512.0f;
-  const uint32_t sub = (uint32_t)__builtin_rintf(sub_steps);
-  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-  uint32_t code = a < 0x3C800000u ? sub : (r >> 20) - (120u << 3);
-  code = a >= 0x43E00000u ? 0x7Eu : code;  // |p| >= 448
-  code |= sign;
-  return a > 0x7F800000u ? 0x7Fu : code;   // NaN
+// fp32 -> OCP e4m3 ("e4m3fn") codes, round to nearest even, saturating to
+// +-448; the infinities saturate and every NaN gives 0x7F. Four values per
+// call, packed little-endian into one word. The conversion itself is the
+// gfx950 instruction v_cvt_pk_fp8_f32 (OCP e4m3, round to nearest even) on
+// inputs clamped to [-448, 448] first, so that nothing reaches its overflow
+// handling; NaN inputs are patched to 0x7F afterwards (rare: a scalar branch
+// skips the patch when no lane has one).
+__device__ __forceinline__ uint32_t e4m3_code4(float p0, float p1, float p2, float p3) {
+  const float c0 = __builtin_amdgcn_fmed3f(p0, -448.0f, 448.0f);
+  const float c1 = __builtin_amdgcn_fmed3f(p1, -448.0f, 448.0f);
+  const float c2 = __builtin_amdgcn_fmed3f(p2, -448.0f, 448.0f);
+  const float c3 = __builtin_amdgcn_fmed3f(p3, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  uint32_t code = (uint32_t)w;
+  const bool n0 = p0 != p0, n1 = p1 != p1, n2 = p2 != p2, n3 = p3 != p3;
+  if (__builtin_expect(n0 || n1 || n2 || n3, 0)) {
+    const uint32_t m = (n0 ? 0xFFu : 0u) | (n1 ? 0xFF00u : 0u) | (n2 ? 0xFF0000u : 0u) |
+                       (n3 ? 0xFF000000u : 0u);
+    code = (code & ~m) | (0x7F7F7F7Fu & m);
+  }
+  return code;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -105,11 +108,8 @@ __device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, c
     inv = 448.0f / amax;
     scale = amax / 448.0f;
   }
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) lo |= e4m3_code(f[j] * inv) << (8 * j);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hi |= e4m3_code(f[4 + j] * inv) << (8 * j);
+  const uint32_t lo = e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+  const uint32_t hi = e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
   *reinterpret_cast<uint2*>(msg + 4 + 8 * u) = make_uint2(lo, hi);
   if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = scale;
 }
@@ -145,142 +145,175 @@ __device__ __forceinline__ void stage_fp8(uint8_t* msg, const u32x4* __restrict_
   }
 }
 
-template <int DT, int MAXK>
+// Row t of x (first kStage * blockDim chunks) into registers; unconditional
+// loads with the index clamped into the row.
+template <int NSTAGE>
+__device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __restrict__ xr,
+                                         int chunks) {
+#pragma unroll
+  for (int u = 0; u < NSTAGE; ++u) {
+    const int j = (int)threadIdx.x + u * (int)blockDim.x;
+    r[u] = xr[j < chunks ? j : chunks - 1];
+  }
+}
+
+// message(t) into an LDS buffer: header, then the bf16 row or its fp8 form.
+// r holds the row's first round of loads.
+template <int DT, int NSTAGE>
+__device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* __restrict__ xr,
+                                              int hidden, const u32x4 (&r)[NSTAGE]) {
+  const int tid = threadIdx.x;
+  const int B = blockDim.x;
+  const int chunks = hidden / 8;
+  if (tid == 0) *reinterpret_cast<int32_t*>(msg) = t;
+  if (DT == kBf16) {
+#pragma unroll
+    for (int u = 0; u < NSTAGE; ++u) {
+      const int j = tid + u * B;
+      if (j < chunks) *reinterpret_cast<u32x4*>(msg + 4 + 16 * j) = r[u];
+    }
+    for (int j0 = tid + NSTAGE * B; j0 < chunks; j0 += NSTAGE * B) {
+      u32x4 q[NSTAGE];
+#pragma unroll
+      for (int u = 0; u < NSTAGE; ++u) {
+        const int j = j0 + u * B;
+        q[u] = xr[j < chunks ? j : chunks - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < NSTAGE; ++u) {
+        const int j = j0 + u * B;
+        if (j < chunks) *reinterpret_cast<u32x4*>(msg + 4 + 16 * j) = q[u];
+      }
+    }
+  } else {
+    stage_fp8<NSTAGE>(msg, xr, hidden, r);
+  }
+}
+
+// One message from LDS to its destination: 0-3 head dwords and 0-3 tail
+// dwords (two threads), then 16-byte body chunks, four per thread per round
+// with the round's LDS reads issued before its stores; destination-aligned,
+// device-coherent stores confined to the message by the buffer descriptor.
+__device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32_t md) {
+  constexpr int kCopy = 4;
+  const uint32_t tid = threadIdx.x;
+  const BufRsrc rsrc = message_rsrc(d, md);
+  const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
+  const uint32_t nb = (md - head) >> 4;
+  const uint32_t body_end = head + 16u * nb;
+  if (tid == 0)
+    for (uint32_t b = 0; b < head; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
+  if (tid == 1)
+    for (uint32_t b = body_end; b < md; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
+  for (uint32_t i0 = tid; i0 < nb; i0 += kCopy * blockDim.x) {
+    u32x4_a4 v[kCopy];
+#pragma unroll
+    for (int u = 0; u < kCopy; ++u) {
+      const uint32_t i = i0 + u * blockDim.x;
+      v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < nb ? i : nb - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < kCopy; ++u) {
+      const uint32_t i = i0 + u * blockDim.x;
+      if (i < nb) store_b128(v[u], rsrc, head + 16u * i);
+    }
+  }
+}
+
+template <int DT>
 __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const DispatchParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ RouteShared rs;
-  __shared__ uint64_t s_dst[MAXK + 1];
-  __shared__ int s_nmsg;
 
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
     for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
 
-  const int t = blockIdx.x / P.groups;
-  const int g = blockIdx.x - t * P.groups;
-  if (t >= P.num_tokens) return;
-
-  // 1. issue the loads of x[t] (first staging round) before the routing
-  //    prologue so that both memory round trips overlap
-  uint8_t* msg = lds_raw + kMsgLdsOffset;
-  const u32x4* xr = reinterpret_cast<const u32x4*>(P.x) + (size_t)t * (P.hidden / 8);
+  // workgroup -> (tile of tokens [t0, t1), message group g)
+  const int tile = blockIdx.x / P.groups;
+  const int g = blockIdx.x - tile * P.groups;
+  const int t0 = tile * P.tile;
+  if (t0 >= P.num_tokens) return;
+  const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
+  const int K = P.topk;
   const int chunks = P.hidden / 8;
+  const uint32_t md = P.msg_bytes;
+  const u32x4* x = reinterpret_cast<const u32x4*>(P.x);
+  auto message_buffer = [&](int i) {
+    return lds_raw + (P.nbuf == 2 ? (i & 1) : 0) * P.msg_stride + kMsgLdsOffset;
+  };
+
+  // 1. loads of x[t0] first, then the routing prologue; message(t0) is
+  //    built in LDS while the routing loads are in flight
   constexpr int kStage = 4;
   u32x4 r[kStage];
-#pragma unroll
-  for (int u = 0; u < kStage; ++u) {
-    const int j = tid + u * (int)blockDim.x;
-    r[u] = xr[j < chunks ? j : chunks - 1];  // unconditional: one wait for all
-  }
+  load_row<kStage>(r, x + (size_t)t0 * chunks, chunks);
+  route_tile(P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs, [&]() {
+    build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
+  });
 
-  // 2. slots of token t
-  route_token<MAXK>(P.idx, t, P.topk, P.num_experts, P.max_tokens, rs);
-
-  // 3. message(t) in LDS: the preloaded round, then (rows longer than
-  //    kStage * blockDim chunks only) the remaining rounds
-  if (tid == 0) *reinterpret_cast<int32_t*>(msg) = t;
-  if (DT == kBf16) {
-#pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-      const int j = tid + u * (int)blockDim.x;
-      if (j < chunks) *reinterpret_cast<u32x4*>(msg + 4 + 16 * j) = r[u];
+  // 2. per token: build message(t) (double-buffered, so one barrier), fetch
+  //    x[t + 1] while the stores of t go out, and write message(t) to the
+  //    destinations of this group: m = g, g + groups, ..., where m == topk
+  //    is the send row and a masked pick has none
+  for (int t = t0; t < t1; ++t) {
+    const int i = t - t0;
+    uint8_t* msg = message_buffer(i);
+    if (i > 0) {
+      if (P.nbuf == 1) __syncthreads();  // the single buffer is still being read
+      build_message<DT, kStage>(msg, t, x + (size_t)t * chunks, P.hidden, r);
+      __syncthreads();
     }
-    for (int j0 = tid + kStage * (int)blockDim.x; j0 < chunks; j0 += kStage * (int)blockDim.x) {
-      u32x4 q[kStage];
-#pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int j = j0 + u * (int)blockDim.x;
-        q[u] = xr[j < chunks ? j : chunks - 1];
+    if (t + 1 < t1) load_row<kStage>(r, x + (size_t)(t + 1) * chunks, chunks);
+    for (int m = g; m <= K; m += P.groups) {
+      uint8_t* d;
+      if (m == K) {
+        d = P.send + (uint64_t)t * md;
+      } else {
+        const int s = rs.slot[i * K + m];
+        if (s < 0) continue;
+        d = P.recv + ((uint64_t)rs.expert[i * K + m] * (uint64_t)P.max_tokens + (uint64_t)s) * md;
       }
-#pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int j = j0 + u * (int)blockDim.x;
-        if (j < chunks) *reinterpret_cast<u32x4*>(msg + 4 + 16 * j) = q[u];
-      }
-    }
-  } else {
-    stage_fp8<kStage>(msg, xr, P.hidden, r);
-  }
-
-  // 4. this workgroup's destinations: message m = g, g + groups, ... where
-  //    m == topk is the send row (its barrier also publishes the LDS message)
-  if (tid == 0) {
-    int n = 0;
-    for (int m = g; m <= P.topk; m += P.groups) {
-      if (m == P.topk) {
-        s_dst[n++] = (uint64_t)(P.send + (uint64_t)t * P.msg_bytes);
-      } else if (rs.slot[m] >= 0) {
-        const uint64_t row = (uint64_t)rs.expert[m] * (uint64_t)P.max_tokens + (uint64_t)rs.slot[m];
-        s_dst[n++] = (uint64_t)(P.recv + row * P.msg_bytes);
-      }
-    }
-    s_nmsg = n;
-  }
-  __syncthreads();
-
-  // 5. stream LDS -> destinations with destination-aligned 16-byte stores.
-  //    Per message: 0-3 head dwords and 0-3 tail dwords (one thread each),
-  //    then the 16-byte body chunks, four per thread per round with the LDS
-  //    reads of a round issued before its stores.
-  const int nmsg = s_nmsg;
-  const uint32_t md = P.msg_bytes;
-  if (tid < nmsg) {
-    void* d = reinterpret_cast<void*>(s_dst[tid]);
-    const BufRsrc r = message_rsrc(d, md);
-    const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
-    const uint32_t body_end = head + ((md - head) & ~15u);
-    for (uint32_t b = 0; b < head; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), r, b);
-    for (uint32_t b = body_end; b < md; b += 4)
-      store_b32(*reinterpret_cast<const uint32_t*>(msg + b), r, b);
-  }
-  constexpr int kCopy = 4;
-  for (int mi = 0; mi < nmsg; ++mi) {
-    void* d = reinterpret_cast<void*>(s_dst[mi]);
-    const BufRsrc r = message_rsrc(d, md);
-    const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
-    const uint32_t nb = (md - head) >> 4;
-    for (uint32_t i0 = tid; i0 < nb; i0 += kCopy * blockDim.x) {
-      u32x4_a4 v[kCopy];
-#pragma unroll
-      for (int u = 0; u < kCopy; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
-        v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < nb ? i : nb - 1));
-      }
-#pragma unroll
-      for (int u = 0; u < kCopy; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
-        if (i < nb) store_b128(v[u], r, head + 16u * i);
-      }
+      copy_message(d, msg, md);
     }
   }
-  // every wave waits until its own device-coherent stores are complete;
-  // after the barrier, all of this workgroup's messages are visible at
-  // device scope
+
+  // 3. every wave waits until its own device-coherent stores are complete;
+  //    after the barrier, all of this workgroup's messages are visible at
+  //    device scope
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
-  // 6. publish: one device-scope add per routed pick of this workgroup.
+  // 4. publish: per wavefront-chunk of the tile's entries, one device-scope
+  //    add per expert this workgroup wrote to, of its number of messages.
   //    The messages were written with device-coherent stores that have all
-  //    completed (step 5), so the adds need no cache write-back of their
+  //    completed (step 3), so the adds need no cache write-back of their
   //    own: a reader that loads the count with acquire semantics at device
   //    scope (which invalidates its L2 copy) sees the messages.
-  if (tid < P.topk && (tid % P.groups) == g && rs.slot[tid] >= 0)
-    __hip_atomic_fetch_add(P.sig + rs.expert[tid], 1ull, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  const int n = (t1 - t0) * K;
+  const int wave = tid / kWave;
+  for (int j0 = wave * kWave; j0 < n; j0 += (int)(blockDim.x / kWave) * kWave) {
+    const int j = j0 + (tid & (kWave - 1));
+    int e = -1;
+    if (j < n) {
+      const int k = j - (j / K) * K;
+      if (k - (k / P.groups) * P.groups == g && rs.slot[j] >= 0) e = rs.expert[j];
+    }
+    int group = 0;  // messages to e from this chunk, on the lowest lane naming e
+    for_each_distinct(e, [&](int v, uint64_t same) {
+      if (e == v && (same & lanes_below()) == 0) group = __popcll(same);
+    });
+    if (group > 0)
+      __hip_atomic_fetch_add(P.sig + e, (unsigned long long)group, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int DT>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
-  const int blocks = p.num_tokens > 0 ? p.num_tokens * p.groups : 1;
-  const size_t lds = ((size_t)kMsgLdsOffset + p.msg_bytes + 15) & ~(size_t)15;
-  if (p.topk <= 2)
-    dispatch_kernel<DT, 2><<<blocks, kDispatchBlock, lds, stream>>>(p);
-  else if (p.topk <= 4)
-    dispatch_kernel<DT, 4><<<blocks, kDispatchBlock, lds, stream>>>(p);
-  else if (p.topk <= 8)
-    dispatch_kernel<DT, 8><<<blocks, kDispatchBlock, lds, stream>>>(p);
-  else
-    dispatch_kernel<DT, 16><<<blocks, kDispatchBlock, lds, stream>>>(p);
+  const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
+  const size_t lds = (size_t)p.nbuf * p.msg_stride;
+  dispatch_kernel<DT><<<tiles * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -288,17 +321,25 @@ hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t strea
   return dtype == kBf16 ? launch_dt<kBf16>(p, stream) : launch_dt<kFp8>(p, stream);
 }
 
-// The fp8 encoder above, applied element-wise; lets a test compare it with
-// an independent encoder on chosen fp32 inputs.
+// The fp8 encoder above, applied element-wise in groups of four; lets a test
+// compare it with an independent encoder on chosen fp32 inputs.
 __global__ void e4m3_probe_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
                                   uint64_t n) {
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (uint64_t)gridDim.x * blockDim.x)
-    out[i] = (uint8_t)e4m3_code(in[i]);
+  const uint64_t groups = (n + 3) / 4;
+  for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+       g += (uint64_t)gridDim.x * blockDim.x) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = 4 * g + j < n ? in[4 * g + j] : 0.0f;
+    const uint32_t code = e4m3_code4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * g + j < n) out[4 * g + j] = (uint8_t)(code >> (8 * j));
+  }
 }
 
 hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, hipStream_t stream) {
-  uint64_t blocks = (n + 255) / 256;
+  uint64_t blocks = ((n + 3) / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks == 0) blocks = 1;
   e4m3_probe_kernel<<<(unsigned)blocks, 256, 0, stream>>>(in, out, n);

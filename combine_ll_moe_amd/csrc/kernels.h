@@ -19,8 +19,11 @@ struct DispatchParams {
   int hidden;
   int num_experts;
   int topk;
-  int groups;                      // workgroups per token (each takes every groups-th message)
+  int tile;                        // consecutive tokens per workgroup
+  int groups;                      // workgroups per tile (each takes every groups-th message)
   uint32_t msg_bytes;              // md
+  uint32_t msg_stride;             // bytes of one LDS message buffer
+  int nbuf;                        // LDS message buffers (2: double-buffered)
 };
 
 struct CombineParams {
@@ -34,8 +37,19 @@ struct CombineParams {
   int hidden;
   int num_experts;
   int topk;
-  int slices;                      // workgroups per token, each a contiguous run of columns
+  int tile;                        // consecutive tokens per workgroup
+  int slices;                      // workgroups per tile, each a contiguous run of columns
 };
+
+// LDS placement of a message: it starts at this offset of its buffer, so
+// that the payload (message byte 4) is 16-byte aligned; a buffer is
+// kMsgLdsOffset + md rounded up to 16 bytes.
+constexpr int kMsgLdsOffset = 12;
+constexpr int kDispatchBlock = 256;
+constexpr int kCombineBlock = 256;
+// LDS a dispatch workgroup may use for message buffers: 64 KiB less the
+// routing prologue's static share.
+constexpr uint32_t kDispatchLdsBudget = 65536 - 18432;
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

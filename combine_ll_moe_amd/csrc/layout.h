@@ -15,7 +15,7 @@ namespace llmoe {
 enum : int { kBf16 = 0, kFp8 = 1 };
 constexpr int kFp8Block = 128;
 constexpr int kMaxTopk = 16;
-constexpr uint64_t kMaxMessageBytes = 61440;
+constexpr uint64_t kMaxMessageBytes = 45056;
 
 struct Layout {
   uint64_t dispatch_msg;  // md

@@ -5,19 +5,19 @@
 // receive buffer); expert e owns rows [e * max_tokens, (e + 1) * max_tokens).
 // A routed entry (t, k) goes to row e * max_tokens + slot(t, k), where
 // slot(t, k) counts the earlier entries, in (t, k) order, that name the same
-// expert: the entries of tokens before t, plus the picks of t itself before
-// k. That is an exclusive prefix count per expert in ascending token order,
-// which makes the slot order deterministic.
+// expert. That is an exclusive prefix count per expert in ascending token
+// order, which makes the slot order deterministic.
 //
-// Every workgroup that serves token t recomputes the slots of t from the
-// routing table itself (no workspace, no second launch): the table is at
-// most a few tens of KiB and stays in L2.
-//  - Up to kHistExperts experts: a per-expert histogram of the earlier
-//    tokens' entries in LDS, one LDS atomic per entry whatever topk is.
-//  - More experts: a ballot per (entry, pick) over the earlier entries,
-//    summed across the wavefronts in LDS.
-// Loads are unconditional (indices clamped into the table, clamped lanes
-// masked afterwards), so the compiler issues them back to back.
+// A workgroup serves a tile of consecutive tokens [t0, t1) and computes the
+// slots of all the tile's entries at once from the routing table itself (no
+// workspace, no second launch; the table is a few tens of KiB and stays in
+// L2):
+//   slot(j) = (entries before the tile naming e)      an LDS histogram
+//           + (tile entries before j naming e)        a short LDS loop
+// The histogram covers kHistExperts experts per pass; more experts take
+// more passes over the earlier entries. Loads are unconditional (indices
+// clamped into the table, clamped lanes masked afterwards), so the compiler
+// issues them back to back.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,38 +28,71 @@
 namespace llmoe {
 
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 16;
 constexpr int kHistExperts = 4096;
+constexpr int kMaxTileEntries = 256;  // tokens per tile * topk
 
 struct RouteShared {
-  alignas(16) int expert[kMaxTopk];  // idx[t, k]
-  alignas(16) int slot[kMaxTopk];    // slot(t, k), or -1 when the entry is masked
-  int partial[kMaxWaves][kMaxTopk];
+  int expert[kMaxTileEntries];  // idx of the tile's entries, tile order
+  int slot[kMaxTileEntries];    // their slots, or -1 when masked
   int hist[kHistExperts];
 };
 
+struct NoOverlap {
+  __device__ void operator()() const {}
+};
+
+// Mask of the lanes below this one in its wavefront.
+__device__ __forceinline__ uint64_t lanes_below() {
+  return (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
+}
+
+// Wavefront-wide grouping by value: for each distinct value v >= 0 held by
+// the active lanes, calls f(v, mask of lanes holding v) on every lane (the
+// loop is uniform). The loop runs once per distinct value, without memory.
+template <typename F>
+__device__ __forceinline__ void for_each_distinct(int value, const F& f) {
+  uint64_t left = __ballot(value >= 0);
+  while (left) {
+    const int leader = __builtin_ctzll(left);
+    const int v = __builtin_amdgcn_readlane(value, leader);
+    const uint64_t same = __ballot(value == v);
+    f(v, same);
+    left &= ~same;
+  }
+}
+
 // All threads of the workgroup must call this (it contains barriers).
-// On return rs.expert[k] and rs.slot[k] hold token t's picks and slots for
-// k < topk. blockDim.x must be a multiple of 64 and at most 1024, and
-// 1 <= topk <= MAXK <= kMaxTopk.
-template <int MAXK>
-__device__ __forceinline__ void route_token(const int32_t* __restrict__ idx, int t, int topk,
-                                            int num_experts, int max_tokens, RouteShared& rs) {
+// On return rs.expert[j] and rs.slot[j] hold entry j = (t - t0) * topk + k
+// of the tile for t0 <= t < t1. Requires (t1 - t0) * topk <= kMaxTileEntries.
+// `overlap()` runs once on every thread while the first pass's loads are in
+// flight, before a barrier that both results share (the dispatch builds its
+// first LDS message there).
+//
+// Slots within the tile: an entry's slot is the histogram count of its
+// expert plus its rank among the tile's earlier entries naming the same
+// expert. Up to 64 entries this is a register walk in wavefront 0; beyond,
+// wavefront 0 walks 64 entries at a time, keeping running counts in LDS.
+template <typename Overlap = NoOverlap>
+__device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
+                                           int topk, int num_experts, int max_tokens,
+                                           RouteShared& rs, const Overlap& overlap = Overlap()) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int nthreads = blockDim.x;
-  const int first = t * topk;  // entries of earlier tokens: [0, first)
+  const int first = t0 * topk;         // entries before the tile: [0, first)
+  const int n = (t1 - t0) * topk;      // the tile's entries: [first, first + n)
   constexpr int kUnroll = 8;
 
-  // the token's own picks (uniform; picks past topk repeat the last one and
-  // are never used)
-  int pick[MAXK];
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) pick[k] = idx[first + (k < topk ? k : topk - 1)];
+  // the tile's own entries, loaded with the scan's (threads j < n); for a
+  // tile of up to 64 entries they stay in wavefront 0's registers
+  const int mine = tid < n ? idx[first + tid] : -1;
+  if (tid < n) {
+    rs.expert[tid] = mine;
+    rs.slot[tid] = -1;
+  }
 
-  if (num_experts <= kHistExperts) {
-    for (int e = tid; e < num_experts; e += nthreads) rs.hist[e] = 0;
+  for (int c0 = 0; c0 < num_experts; c0 += kHistExperts) {  // uniform
+    const int width = num_experts - c0 < kHistExperts ? num_experts - c0 : kHistExperts;
+    for (int i = tid; i < width; i += nthreads) rs.hist[i] = 0;
     __syncthreads();
     const int last = first > 0 ? first - 1 : 0;
     for (int base = tid; base < first; base += nthreads * kUnroll) {
@@ -72,64 +105,49 @@ __device__ __forceinline__ void route_token(const int32_t* __restrict__ idx, int
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int p = base + u * nthreads;
-        if (p < first && v[u] >= 0 && v[u] < num_experts) atomicAdd(&rs.hist[v[u]], 1);
+        const unsigned rel = (unsigned)v[u] - (unsigned)c0;
+        if (p < first && rel < (unsigned)width) atomicAdd(&rs.hist[rel], 1);
+      }
+    }
+    if (c0 == 0) overlap();
+    __syncthreads();
+    if (n <= kWave) {
+      // one chunk: rank = earlier lanes with the same expert (register walk)
+      if (tid < kWave) {
+        const unsigned rel = (unsigned)mine - (unsigned)c0;
+        const bool here = tid < n && rel < (unsigned)width;
+        int rank = 0;
+        for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
+        if (here) {
+          const int s = rs.hist[rel] + rank;
+          rs.slot[tid] = s < max_tokens ? s : -1;
+        }
+      }
+    } else if (tid < kWave) {
+      // 64 entries at a time, in order: the running count of each expert is
+      // the histogram plus the chunks already walked
+      for (int j0 = 0; j0 < n; j0 += kWave) {  // uniform in wavefront 0
+        const int j = j0 + tid;
+        const int e = j < n ? rs.expert[j] : -1;
+        const unsigned rel = (unsigned)e - (unsigned)c0;
+        const bool here = j < n && rel < (unsigned)width;
+        const int base_count = here ? rs.hist[rel] : 0;
+        int rank = 0, group = 0;
+        for_each_distinct(here ? (int)rel : -1, [&](int v, uint64_t same) {
+          if (here && (int)rel == v) {
+            rank = __popcll(same & lanes_below());
+            group = __popcll(same);
+          }
+        });
+        if (here) {
+          const int s = base_count + rank;
+          rs.slot[j] = s < max_tokens ? s : -1;
+          if (rank == 0) rs.hist[rel] += group;  // the lowest lane of each value
+        }
       }
     }
     __syncthreads();
-    if (tid < topk) {
-      int e = pick[0];  // this thread's pick, and how often it came earlier in t
-      int same = 0;
-#pragma unroll
-      for (int k = 0; k < MAXK; ++k) e = k == tid ? pick[k] : e;
-#pragma unroll
-      for (int k = 0; k < MAXK; ++k) same += (k < tid) & (pick[k] == e);
-      const bool valid = e >= 0 && e < num_experts;
-      const int s = valid ? rs.hist[e] + same : 0;
-      rs.expert[tid] = e;
-      rs.slot[tid] = valid && s < max_tokens ? s : -1;
-    }
-    __syncthreads();
-    return;
   }
-
-  // many experts: one ballot per (entry, pick); entry p counts for pick k
-  // when it names the same expert and comes before (t, k): p < first + k
-  const int end = first + topk;
-  const int last = end - 1;
-  int cnt[MAXK];  // wave-uniform
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) cnt[k] = 0;
-  for (int base = wave * kWave; base < end; base += nthreads * kUnroll) {
-    int v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + lane + u * nthreads;
-      v[u] = idx[p < last ? p : last];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int p = base + lane + u * nthreads;
-#pragma unroll
-      for (int k = 0; k < MAXK; ++k) cnt[k] += __popcll(__ballot(v[u] == pick[k] && p < first + k));
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) rs.partial[wave][k] = cnt[k];
-  }
-  if (tid == 0) {
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) rs.expert[k] = pick[k];
-  }
-  __syncthreads();
-  if (tid < topk) {
-    int s = 0;
-    for (int w = 0; w < nthreads / kWave; ++w) s += rs.partial[w][tid];
-    const int e = rs.expert[tid];
-    const bool routed = e >= 0 && e < num_experts && s < max_tokens;
-    rs.slot[tid] = routed ? s : -1;
-  }
-  __syncthreads();
 }
 
 }  // namespace llmoe

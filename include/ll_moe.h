@@ -28,9 +28,10 @@
  *     anything is enqueued and leave every buffer untouched. Errors in the
  *     data (expert ids) are not errors: see "routing" below.
  *   - Workloads: max_tokens >= 1, 0 <= num_tokens <= max_tokens,
- *     1 <= topk <= min(num_experts, LL_MOE_MAX_TOPK); bf16 needs
- *     hidden % 8 == 0, fp8 needs hidden % 128 == 0; a dispatch message may
- *     not exceed LL_MOE_MAX_MESSAGE_BYTES.
+ *     1 <= topk <= min(num_experts, LL_MOE_MAX_TOPK),
+ *     num_experts <= LL_MOE_MAX_EXPERTS, max_tokens * topk < 2^31; bf16
+ *     needs hidden % 8 == 0, fp8 needs hidden % 128 == 0; a dispatch message
+ *     may not exceed LL_MOE_MAX_MESSAGE_BYTES (bf16: hidden <= 22520).
  *
  * Routing (topk_idx, int32 [num_tokens, topk], row-major):
  *   Entry (t, k) names the expert of token t's k-th pick. Expert e owns the
@@ -76,7 +77,8 @@ typedef enum {
 } ll_moe_status_t;
 
 #define LL_MOE_MAX_TOPK 16
-#define LL_MOE_MAX_MESSAGE_BYTES 61440
+#define LL_MOE_MAX_MESSAGE_BYTES 45056
+#define LL_MOE_MAX_EXPERTS (1 << 20)
 
 /*
  * ll_moe_layout_bytes — bytes of one layout (both buffer sets).

@@ -68,7 +68,7 @@ FAKE = 0x10000  # never dereferenced: every case below fails validation first
     dict(topk=0), dict(topk=9, num_experts=8), dict(topk=17, num_experts=64),
     dict(hidden=1020), dict(dtype=1, hidden=1000), dict(dtype=7), dict(layout=0),
     dict(layout=FAKE + 8), dict(x=0), dict(x=FAKE + 4), dict(idx=0), dict(idx=FAKE + 2),
-    dict(max_tokens=0), dict(hidden=8 * 4000),
+    dict(max_tokens=0), dict(hidden=8 * 2816), dict(num_experts=(1 << 20) + 1),
 ])
 def test_dispatch_rejects_bad_arguments(case):
     import combine_ll_moe_amd as ll
