@@ -24,6 +24,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HOLD_CYCLES = 5_000_000
 
 
 def algorithmic_bytes(w, md: int, routed: int) -> dict:
@@ -36,6 +37,121 @@ def algorithmic_bytes(w, md: int, routed: int) -> dict:
     dispatch = n * h * 2 + 4 * n * k + n * md + routed * md + 8 * e + 8 * e
     combine = 8 * n * k + routed * h * 2 + 4 * n * h + 8 * e
     return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine}
+
+
+KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}
+COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                             "hbm_counters.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; stored counters apply only to the same code."""
+    import glob
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_ll_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(root, "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the stored FETCH_SIZE / WRITE_SIZE counters,
+    each scaled by what the counter read for a plain copy of known size; None
+    when there are none for this workload or the kernels changed since."""
+    try:
+        with open(COUNTERS_JSON) as f:
+            c = json.load(f)
+    except OSError:
+        return None
+    if c.get("source_sha256") != kernel_source_hash():
+        return None
+    k = c.get("workloads", {}).get(workload, {}).get(kernel)
+    if not k:
+        return None
+    cp = c["copy"]
+    f_fetch = cp["fetch_kib"] * 1024.0 / cp["bytes"]
+    f_write = cp["write_kib"] * 1024.0 / cp["bytes"]
+    return round(k["fetch_kib"] * 1024.0 / f_fetch + k["write_kib"] * 1024.0 / f_write)
+
+
+def _counter_means(path: str, counter: str) -> dict:
+    import csv
+    import collections
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_profiles(args) -> None:
+    """Turn rocprofv3 CSV output into the committed summaries under profiles/:
+    a markdown table per workload and the counters file bench.py reads."""
+    import csv
+    prof = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+    os.makedirs(prof, exist_ok=True)
+    stats = list(csv.DictReader(open(args.trace)))
+    fetch = _counter_means(args.fetch, "FETCH_SIZE")
+    write = _counter_means(args.write, "WRITE_SIZE")
+    cfetch = _counter_means(args.copy_fetch, "FETCH_SIZE")
+    cwrite = _counter_means(args.copy_write, "WRITE_SIZE")
+    copies = [k for k in cwrite if "copy" in k.lower()]  # the probe's copy kernel
+    copy_name = max(copies, key=lambda k: cwrite[k])
+    copy = {"bytes": args.copy_bytes, "kernel": copy_name,
+            "fetch_kib": round(cfetch[copy_name], 1), "write_kib": round(cwrite[copy_name], 1)}
+    per = {}
+    for short, name in KERNEL_NAMES.items():
+        fk = [k for k in fetch if name in k]
+        wk = [k for k in write if name in k]
+        if fk and wk:
+            per[short] = {"kernel": fk[0], "fetch_kib": round(fetch[fk[0]], 1),
+                          "write_kib": round(write[wk[0]], 1)}
+    try:
+        with open(COUNTERS_JSON) as f:
+            c = json.load(f)
+    except OSError:
+        c = {}
+    if c.get("source_sha256") != kernel_source_hash():
+        c = {"workloads": {}}
+    c["source_sha256"] = kernel_source_hash()
+    c["copy"] = copy
+    c.setdefault("workloads", {})[args.workload] = per
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(c, f, indent=1, sort_keys=True)
+
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    md = (4 + 2 * w.hidden) if w.dtype == W.BF16 else (4 + w.hidden + w.hidden // 32)
+    ab = algorithmic_bytes(w, md, w.num_tokens * w.topk)
+    f_fetch = copy["fetch_kib"] * 1024.0 / copy["bytes"]
+    f_write = copy["write_kib"] * 1024.0 / copy["bytes"]
+    lines = [f"# {args.workload}: dispatch and combine kernels (rocprofv3)", "",
+             f"Workload: {w.name}, N={w.num_tokens}, hidden={w.hidden}, experts={w.num_experts}, "
+             f"top-k={w.topk}, payload {'bf16' if w.dtype == W.BF16 else 'fp8 e4m3'}.", "",
+             "## Kernel durations (`--kernel-trace --stats`)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## HBM bytes per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
+              f"Calibration: a plain {copy['bytes']} B device copy (`{copy_name[:60]}`) read "
+              f"FETCH_SIZE {copy['fetch_kib']} KiB and WRITE_SIZE {copy['write_kib']} KiB, "
+              f"factors {f_fetch:.3f} and {f_write:.3f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|"]
+    for short, k in per.items():
+        hbm = k["fetch_kib"] * 1024 / f_fetch + k["write_kib"] * 1024 / f_write
+        lines.append(f"| {short} | {k['fetch_kib']} | {k['write_kib']} | {hbm:.0f} | {ab[short]} | "
+                     f"{hbm / ab[short]:.3f} |")
+    lines += ["", "## Commands", "", "```"] + args.commands + ["```", ""]
+    out = os.path.join(prof, f"ll_moe_{args.workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -75,7 +191,35 @@ def main():
                     help="distinct input batches cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--summarize-profiles", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 CSV files (no GPU)")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES five times "
+                         "(calibrates the HBM byte counters against a known size)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(args)
+        return
+
+    if args.copy_probe:
+        import torch
+        a = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[copy-probe] copied {args.copy_probe} bytes 5 times", file=sys.stderr)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -132,10 +276,18 @@ def main():
         combine(s)
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps, nothing else on the stream
+    # The host enqueues launches more slowly than the GPU runs them at these
+    # sizes, so a short spin kernel first holds the stream while the timed
+    # launches are queued behind it: the events then time the GPU running
+    # the steps back to back, not the host's launch rate.
+    def hold_stream():
+        torch.cuda._sleep(HOLD_CYCLES)
+
+    # timed region: K back-to-back steps, nothing else between them
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold_stream()
     t0.record(stream)
     for s in range(args.steps):
         dispatch(s)
@@ -146,23 +298,53 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
           flush=True)
 
-    # per-kernel launch times: the same steps with an event pair around each
-    # launch, on the stream the kernels run on
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        e = ev[s]
-        e[0].record(stream)
-        dispatch(s)
-        e[1].record(stream)
-        e[2].record(stream)
-        combine(s)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    d_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-    c_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
+    # per-kernel launch times: K launches of one kernel back to back (parity
+    # alternating, as in the step), timed on the stream they run on
+    def time_kernel(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold_stream()
+        a.record(stream)
+        for s in range(args.steps):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / args.steps
+
+    d_us = time_kernel(dispatch)
+    c_us = time_kernel(combine)
     print(f"[bench] dispatch {d_us:.2f} us/launch, combine {c_us:.2f} us/launch",
           file=sys.stderr, flush=True)
+
+    # the same K steps captured once as a HIP graph and replayed
+    graph_us = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                gs = torch.cuda.current_stream().cuda_stream
+                for s in range(args.steps):
+                    x, idx, wt = batches[s % len(batches)]
+                    ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                       w.topk, w.dtype, s & 1, x, idx, gs)
+                    ll.ll_moe_combine(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                      w.topk, w.dtype, s & 1, y, idx, wt, out, gs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / args.steps
+            best = us if best is None else min(best, us)
+        graph_us = best
+        print(f"[bench] graph replay: {graph_us:.2f} us/step", file=sys.stderr, flush=True)
 
     ab = algorithmic_bytes(w, md, routed[0])
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
@@ -191,10 +373,12 @@ def main():
                    "algorithmic_bytes_per_step": ab["total"]},
         "fraction_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernels_us": {"dispatch": round(d_us, 3), "combine": round(c_us, 3)},
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": ab[dom]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(w.name, dom),
+                     "bytes_per_launch": ab[dom], "us_per_launch": round(dom_us, 3)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
