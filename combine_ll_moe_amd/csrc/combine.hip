@@ -25,6 +25,7 @@
 #include "route.h"
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace llmoe {
 
@@ -32,7 +33,7 @@ namespace llmoe {
 // columns. A masked pick borrows a routed pick's row address so that the
 // loads stay unconditional; its value is never used, and a token with no
 // routed pick reads nothing.
-template <int MAXK>
+template <int MAXK, bool STREAM>
 __device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs, int t,
                                               int i, int c, int chunks) {
   const u32x4* y = reinterpret_cast<const u32x4*>(P.y);
@@ -61,7 +62,10 @@ __device__ __forceinline__ void combine_token(const CombineParams& P, const Rout
   if (any) {
     u32x4 v[MAXK];
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) v[k] = y[(routed[k] ? row[k] : fallback) * (uint64_t)chunks + c];
+    for (int k = 0; k < MAXK; ++k) {
+      const u32x4* src = y + (routed[k] ? row[k] : fallback) * (uint64_t)chunks + c;
+      v[k] = STREAM ? __builtin_nontemporal_load(src) : *src;
+    }
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
       const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
@@ -74,12 +78,15 @@ __device__ __forceinline__ void combine_token(const CombineParams& P, const Rout
       }
     }
   }
-  float4* o = P.out + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
-  o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  // streaming (non-temporal) stores: the output is not read again here
+  f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
+  const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
+  const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
+  __builtin_nontemporal_store(lo, o);
+  __builtin_nontemporal_store(hi, o + 1);
 }
 
-template <int MAXK>
+template <int MAXK, bool STREAM>
 __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombineParams P) {
   __shared__ RouteShared rs;
   const int tid = threadIdx.x;
@@ -98,20 +105,28 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   const int chunks = P.hidden / 8;
   const int c = sl * blockDim.x + tid;
   if (c >= chunks) return;
-  for (int t = t0; t < t1; ++t) combine_token<MAXK>(P, rs, t, t - t0, c, chunks);
+  for (int t = t0; t < t1; ++t) combine_token<MAXK, STREAM>(P, rs, t, t - t0, c, chunks);
+}
+
+template <bool STREAM>
+static void launch_k(const CombineParams& p, int blocks, hipStream_t stream) {
+  if (p.topk <= 2)
+    combine_kernel<2, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 4)
+    combine_kernel<4, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 8)
+    combine_kernel<8, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else
+    combine_kernel<16, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   const int blocks = tiles * p.slices;
-  if (p.topk <= 2)
-    combine_kernel<2><<<blocks, kCombineBlock, 0, stream>>>(p);
-  else if (p.topk <= 4)
-    combine_kernel<4><<<blocks, kCombineBlock, 0, stream>>>(p);
-  else if (p.topk <= 8)
-    combine_kernel<8><<<blocks, kCombineBlock, 0, stream>>>(p);
+  if (p.stream_rows)
+    launch_k<true>(p, blocks, stream);
   else
-    combine_kernel<16><<<blocks, kCombineBlock, 0, stream>>>(p);
+    launch_k<false>(p, blocks, stream);
   return hipGetLastError();
 }
 

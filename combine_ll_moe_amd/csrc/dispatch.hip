@@ -45,9 +45,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // published. The buffer descriptor covers exactly one message, so a store
 // can never leave it.
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
-constexpr int kCachePolicySc1 = 16;
-constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw-buffer format bits
-constexpr int kWaitVmcnt0 = 0x0F70;       // s_waitcnt vmcnt(0)
 
 __device__ __forceinline__ BufRsrc message_rsrc(void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
@@ -87,6 +84,12 @@ __device__ __forceinline__ uint32_t e4m3_code4(float p0, float p1, float p2, flo
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float a) {
+  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
+  return o > a ? o : a;
+}
+
 // Eight elements (unit u) of the fp8 message; the 16 lanes of a block
 // reduce amax together.
 __device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, const u32x4 raw) {
@@ -98,11 +101,13 @@ __device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, c
     const float a = __builtin_fabsf(f[j]);
     amax = a > amax ? a : amax;
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(amax, off, 16);
-    amax = o > amax ? o : amax;
-  }
+  // max over the 16 lanes of the block by DPP within a row of 16 lanes:
+  // swap pairs, swap halves of quads, mirror halves of the row, mirror the
+  // row; every lane ends with the block's maximum (NaN never wins a compare)
+  amax = dpp_max<0xB1>(amax);   // quad_perm [1,0,3,2]
+  amax = dpp_max<0x4E>(amax);   // quad_perm [2,3,0,1]
+  amax = dpp_max<0x141>(amax);  // row_half_mirror
+  amax = dpp_max<0x140>(amax);  // row_mirror
   float inv = 0.0f, scale = 0.0f;
   if (amax > 0.0f) {
     inv = 448.0f / amax;
@@ -229,9 +234,14 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   if (blockIdx.x == 0)
     for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
 
-  // workgroup -> (tile of tokens [t0, t1), message group g)
-  const int tile = blockIdx.x / P.groups;
-  const int g = blockIdx.x - tile * P.groups;
+  // workgroup -> (tile of tokens [t0, t1), message group g). Workgroups
+  // are dealt to the 8 XCDs round-robin by index; all groups of one tile go
+  // to the same XCD, so the tile's rows of x come from HBM once and the
+  // other groups read them from that XCD's L2.
+  const int xcd = blockIdx.x % kXcds;
+  const int pos = blockIdx.x / kXcds;
+  const int tile = xcd + kXcds * (pos / P.groups);
+  const int g = pos - (pos / P.groups) * P.groups;
   const int t0 = tile * P.tile;
   if (t0 >= P.num_tokens) return;
   const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
@@ -312,8 +322,10 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
 template <int DT>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
+  // whole rounds of kXcds tiles, so that the index mapping covers every tile
+  const int rounds = (tiles + kXcds - 1) / kXcds;
   const size_t lds = (size_t)p.nbuf * p.msg_stride;
-  dispatch_kernel<DT><<<tiles * p.groups, kDispatchBlock, lds, stream>>>(p);
+  dispatch_kernel<DT><<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }
 

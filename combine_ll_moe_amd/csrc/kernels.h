@@ -39,6 +39,7 @@ struct CombineParams {
   int topk;
   int tile;                        // consecutive tokens per workgroup
   int slices;                      // workgroups per tile, each a contiguous run of columns
+  int stream_rows;                 // read the expert rows with non-temporal loads
 };
 
 // LDS placement of a message: it starts at this offset of its buffer, so
@@ -46,6 +47,13 @@ struct CombineParams {
 // kMsgLdsOffset + md rounded up to 16 bytes.
 constexpr int kMsgLdsOffset = 12;
 constexpr int kDispatchBlock = 256;
+constexpr int kXcds = 8;  // XCDs of an MI355X; workgroups are dealt to them round-robin
+
+// Buffer-store cache policy with the device-scope coherence bit (sc1): the
+// store writes through the XCD's L2. Raw-buffer descriptor word 3 for gfx9.
+constexpr int kCachePolicySc1 = 16;
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
 constexpr int kCombineBlock = 256;
 // LDS a dispatch workgroup may use for message buffers: 64 KiB less the
 // routing prologue's static share.
