@@ -44,14 +44,19 @@ COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profil
                              "hbm_counters.json")
 
 
+# The sources of the dispatch / combine path (launch shapes included); the
+# diagnostic kernels are not part of it.
+PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "kernels.h", "layout.h", "route.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources; stored counters apply only to the same code."""
-    import glob
+    """Hash of the path's HIP sources; stored counters apply only to the same code."""
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_ll_moe_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(root, "*"))):
-        h.update(os.path.basename(f).encode())
+    for name in PATH_SOURCES:
+        f = os.path.join(root, name)
+        h.update(name.encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -137,6 +142,25 @@ def summarize_profiles(args) -> None:
     for r in stats:
         lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    # the same launches split by bench.py's timed regions: each region starts
+    # with the stream hold (a spin kernel), then steps, dispatch-only and
+    # combine-only loops follow one another
+    trace = list(csv.DictReader(open(args.trace.replace("kernel_stats", "kernel_trace"))))
+    segs, cur = [], None
+    for r in trace:
+        if "spin_kernel" in r["Kernel_Name"]:
+            cur = {}
+            segs.append(cur)
+        elif cur is not None:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            cur.setdefault(r["Kernel_Name"], []).append(d)
+    titles = ["dispatch + combine steps", "dispatch back to back (roofline timing)",
+              "combine back to back (roofline timing)"]
+    lines += ["", "## The same launches by timed region of bench.py", "",
+              "| region | kernel | calls | average us |", "|---|---|---|---|"]
+    for title, seg in zip(titles, segs):
+        for name, ds in seg.items():
+            lines.append(f"| {title} | `{name[:60]}` | {len(ds)} | {sum(ds) / len(ds):.2f} |")
     lines += ["", "## HBM bytes per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
               f"Calibration: a plain {copy['bytes']} B device copy (`{copy_name[:60]}`) read "
               f"FETCH_SIZE {copy['fetch_kib']} KiB and WRITE_SIZE {copy['write_kib']} KiB, "
