@@ -42,10 +42,11 @@ _lib.ll_moe_dispatch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
 _lib.ll_moe_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]
 _lib.ll_moe_clean_signals.argtypes = [_vp, _i, _i, _i, _i, _i, _vp]
 _lib.ll_moe_diag_e4m3.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+_lib.ll_moe_diag_watch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]
 _lib.ll_moe_status_string.argtypes = [_i]
 _lib.ll_moe_status_string.restype = ctypes.c_char_p
 for _f in ("ll_moe_layout_bytes", "ll_moe_layout_offsets", "ll_moe_dispatch",
-           "ll_moe_combine", "ll_moe_clean_signals", "ll_moe_diag_e4m3"):
+           "ll_moe_combine", "ll_moe_clean_signals", "ll_moe_diag_e4m3", "ll_moe_diag_watch"):
     getattr(_lib, _f).restype = _i
 
 
@@ -119,6 +120,17 @@ def ll_moe_clean_signals(layout, max_tokens: int, hidden: int, num_experts: int,
 def ll_moe_diag_e4m3(inp, out, n: int, stream=None) -> None:
     """Diagnostic: the fp8 dispatch's e4m3 encoder applied to n fp32 values."""
     _check(_lib.ll_moe_diag_e4m3(_ptr(inp), _ptr(out), n, _stream(stream)), "ll_moe_diag_e4m3")
+
+
+def ll_moe_diag_watch(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
+                      topk: int, parity: int, x, topk_idx, max_passes: int, report,
+                      stream=None) -> None:
+    """Diagnostic: a concurrent consumer of a bf16 dispatch's counts; report is a
+    zeroed int64[4] (most passes of a workgroup, passes that saw a partial
+    total, violations, last total acquired)."""
+    _check(_lib.ll_moe_diag_watch(_ptr(layout), max_tokens, num_tokens, hidden, num_experts, topk,
+                                  parity, _ptr(x), _ptr(topk_idx), max_passes, _ptr(report),
+                                  _stream(stream)), "ll_moe_diag_watch")
 
 
 def raw_status(name: str, *args) -> int:

@@ -105,6 +105,22 @@ def test_clean_rejects_bad_arguments():
     assert ll.raw_status("ll_moe_diag_e4m3", 0, FAKE, 4, None) == ll.INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", [
+    dict(parity=2), dict(num_tokens=129), dict(topk=0), dict(hidden=1020),
+    dict(num_experts=2049, topk=2), dict(max_passes=0), dict(report=0), dict(report=FAKE + 4),
+    dict(layout=0), dict(x=0), dict(idx=FAKE + 1),
+])
+def test_watch_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
+             parity=0, x=FAKE, idx=FAKE, max_passes=10, report=FAKE)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_diag_watch", a["layout"], a["max_tokens"], a["num_tokens"],
+                       a["hidden"], a["num_experts"], a["topk"], a["parity"], a["x"], a["idx"],
+                       a["max_passes"], a["report"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 def test_binding_routes_through_the_library_only():
     """The binding imports neither the oracle nor the workload generators."""
     src = open(os.path.join(ROOT, "combine_ll_moe_amd", "__init__.py")).read()
