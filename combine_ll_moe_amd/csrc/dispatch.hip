@@ -9,10 +9,12 @@
 // struct mscclppDevConn).
 //
 // Design on gfx950:
-//  - One or more workgroups per token. A workgroup builds message(t) once
-//    in LDS (bf16: a 16-byte-aligned copy of the row; fp8: quantized there),
+//  - One or more workgroups (groups) per token. Each builds message(t) in
+//    LDS (bf16: a 16-byte-aligned copy of the row; fp8: quantized there),
 //    computes the token's slots (route.h), then streams the message from LDS
-//    to each of its destinations.
+//    to its share of the destinations: every groups-th pick's receive row
+//    and an equal part of the send row, so that no group carries a whole
+//    extra message.
 //  - Message rows are 4 + 2h bytes apart, so a destination starts at any
 //    4-byte phase. Stores are aligned to the destination instead: 0-3 head
 //    dwords, then whole 16-byte global_store_dwordx4 chunks, then 0-3 tail
@@ -195,32 +197,38 @@ __device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* 
   }
 }
 
-// One message from LDS to its destination: 0-3 head dwords and 0-3 tail
-// dwords (two threads), then 16-byte body chunks, four per thread per round
-// with the round's LDS reads issued before its stores; destination-aligned,
-// device-coherent stores confined to the message by the buffer descriptor.
-__device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32_t md) {
+// Part `part` of `parts` of one message, from LDS to its destination. The
+// destination splits into 0-3 head dwords, whole 16-byte body chunks and
+// 0-3 tail dwords; part p takes body chunks [nb * p / parts, nb * (p + 1) /
+// parts), the first part also the head and the last the tail (one thread
+// each). Body chunks go four per thread per round, with the round's LDS
+// reads issued before its stores; the stores are destination-aligned,
+// device-coherent, and confined to the message by the buffer descriptor.
+__device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32_t md,
+                                             uint32_t part = 0, uint32_t parts = 1) {
   constexpr int kCopy = 4;
   const uint32_t tid = threadIdx.x;
   const BufRsrc rsrc = message_rsrc(d, md);
   const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
   const uint32_t nb = (md - head) >> 4;
   const uint32_t body_end = head + 16u * nb;
-  if (tid == 0)
+  const uint32_t c0 = nb * part / parts;
+  const uint32_t c1 = nb * (part + 1) / parts;
+  if (part == 0 && tid == 0)
     for (uint32_t b = 0; b < head; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
-  if (tid == 1)
+  if (part == parts - 1 && tid == 1)
     for (uint32_t b = body_end; b < md; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
-  for (uint32_t i0 = tid; i0 < nb; i0 += kCopy * blockDim.x) {
+  for (uint32_t i0 = c0 + tid; i0 < c1; i0 += kCopy * blockDim.x) {
     u32x4_a4 v[kCopy];
 #pragma unroll
     for (int u = 0; u < kCopy; ++u) {
       const uint32_t i = i0 + u * blockDim.x;
-      v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < nb ? i : nb - 1));
+      v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < c1 ? i : c1 - 1));
     }
 #pragma unroll
     for (int u = 0; u < kCopy; ++u) {
       const uint32_t i = i0 + u * blockDim.x;
-      if (i < nb) store_b128(v[u], rsrc, head + 16u * i);
+      if (i < c1) store_b128(v[u], rsrc, head + 16u * i);
     }
   }
 }
@@ -253,19 +261,24 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
     return lds_raw + (P.nbuf == 2 ? (i & 1) : 0) * P.msg_stride + kMsgLdsOffset;
   };
 
-  // 1. loads of x[t0] first, then the routing prologue; message(t0) is
-  //    built in LDS while the routing loads are in flight
+  // 1. the routing prologue; the loads of x[t0] go out with its first
+  //    loads, and message(t0) is built in LDS once they are back
   constexpr int kStage = 4;
   u32x4 r[kStage];
-  load_row<kStage>(r, x + (size_t)t0 * chunks, chunks);
-  route_tile(P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs, [&]() {
-    build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
-  });
+  //    The send row needs no slot: this group's part of it goes out as soon
+  //    as the message is complete, while wavefront 0 computes the slots.
+  route_tile(
+      P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
+      [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
+      [&]() {
+        build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
+      },
+      [&]() { copy_message(P.send + (uint64_t)t0 * md, message_buffer(0), md, g, P.groups); });
 
   // 2. per token: build message(t) (double-buffered, so one barrier), fetch
   //    x[t + 1] while the stores of t go out, and write message(t) to the
-  //    destinations of this group: m = g, g + groups, ..., where m == topk
-  //    is the send row and a masked pick has none
+  //    destinations of this group: part g of the send row, and receive rows
+  //    of the picks m = g, g + groups, ... (a masked pick has none)
   for (int t = t0; t < t1; ++t) {
     const int i = t - t0;
     uint8_t* msg = message_buffer(i);
@@ -273,18 +286,14 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
       if (P.nbuf == 1) __syncthreads();  // the single buffer is still being read
       build_message<DT, kStage>(msg, t, x + (size_t)t * chunks, P.hidden, r);
       __syncthreads();
+      copy_message(P.send + (uint64_t)t * md, msg, md, g, P.groups);
     }
     if (t + 1 < t1) load_row<kStage>(r, x + (size_t)(t + 1) * chunks, chunks);
-    for (int m = g; m <= K; m += P.groups) {
-      uint8_t* d;
-      if (m == K) {
-        d = P.send + (uint64_t)t * md;
-      } else {
-        const int s = rs.slot[i * K + m];
-        if (s < 0) continue;
-        d = P.recv + ((uint64_t)rs.expert[i * K + m] * (uint64_t)P.max_tokens + (uint64_t)s) * md;
-      }
-      copy_message(d, msg, md);
+    for (int m = g; m < K; m += P.groups) {
+      const int s = rs.slot[i * K + m];
+      if (s < 0) continue;
+      copy_message(P.recv + ((uint64_t)rs.expert[i * K + m] * (uint64_t)P.max_tokens + (uint64_t)s) * md,
+                   msg, md);
     }
   }
 

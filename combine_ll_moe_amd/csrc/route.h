@@ -37,6 +37,20 @@ struct RouteShared {
   int hist[kHistExperts];
 };
 
+// Number of lanes below this one in its 16-lane row (DPP row) whose v
+// equals this lane's, for row shifts S..15: each step compares v with the
+// value S lanes lower (row_shr:S); a lane whose source lies outside the row
+// sees -1, which no valid expert equals.
+template <int S>
+__device__ __forceinline__ int same_below_in_row(int v) {
+  if constexpr (S == 16) {
+    return 0;
+  } else {
+    const int o = __builtin_amdgcn_update_dpp(-1, v, 0x110 + S, 0xF, 0xF, false);
+    return (o == v) + same_below_in_row<S + 1>(v);
+  }
+}
+
 struct NoOverlap {
   __device__ void operator()() const {}
 };
@@ -64,43 +78,66 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 // All threads of the workgroup must call this (it contains barriers).
 // On return rs.expert[j] and rs.slot[j] hold entry j = (t - t0) * topk + k
 // of the tile for t0 <= t < t1. Requires (t1 - t0) * topk <= kMaxTileEntries.
-// `overlap()` runs once on every thread while the first pass's loads are in
-// flight, before a barrier that both results share (the dispatch builds its
-// first LDS message there).
+//
+// Every global load of the first pass (the tile's own entries and the first
+// round of earlier entries) is issued before anything waits on one, so the
+// prologue costs one memory round trip, not two. `issue()` runs right after
+// them, so that the caller's own loads travel in the same round trip;
+// `overlap()` runs once on every thread after the first pass's histogram,
+// before a barrier that both results share (the dispatch builds its first
+// LDS message there), and `ready()` on every thread right after that
+// barrier, while wavefront 0 goes on to compute the slots.
 //
 // Slots within the tile: an entry's slot is the histogram count of its
 // expert plus its rank among the tile's earlier entries naming the same
-// expert. Up to 64 entries this is a register walk in wavefront 0; beyond,
+// expert. Up to 16 entries (one DPP row) the rank is 15 row shifts and
+// compares, with no dependent loop; up to 64 it is a register walk in
+// wavefront 0 (also for 1-3 entries, where the walk is shorter); beyond,
 // wavefront 0 walks 64 entries at a time, keeping running counts in LDS.
-template <typename Overlap = NoOverlap>
+template <typename Issue = NoOverlap, typename Overlap = NoOverlap, typename Ready = NoOverlap>
 __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
-                                           RouteShared& rs, const Overlap& overlap = Overlap()) {
+                                           RouteShared& rs, const Issue& issue = Issue(),
+                                           const Overlap& overlap = Overlap(),
+                                           const Ready& ready = Ready()) {
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
   const int first = t0 * topk;         // entries before the tile: [0, first)
   const int n = (t1 - t0) * topk;      // the tile's entries: [first, first + n)
   constexpr int kUnroll = 8;
+  const int stride = nthreads * kUnroll;
+  const int rounds = (first + stride - 1) / stride;  // uniform
+  const int last = first > 0 ? first - 1 : 0;
 
-  // the tile's own entries, loaded with the scan's (threads j < n); for a
-  // tile of up to 64 entries they stay in wavefront 0's registers
-  const int mine = tid < n ? idx[first + tid] : -1;
-  if (tid < n) {
-    rs.expert[tid] = mine;
-    rs.slot[tid] = -1;
+  // loads of the first round and of the tile's own entries (threads j < n;
+  // for a tile of up to 64 entries they stay in wavefront 0's registers);
+  // indices are clamped into the table so the loads are unconditional
+  int v0[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int p = tid + u * nthreads;
+    v0[u] = idx[p < last ? p : last];
   }
+  const int own = idx[first + (tid < n ? tid : 0)];
+  issue();
+  const int mine = tid < n ? own : -1;
 
   for (int c0 = 0; c0 < num_experts; c0 += kHistExperts) {  // uniform
     const int width = num_experts - c0 < kHistExperts ? num_experts - c0 : kHistExperts;
     for (int i = tid; i < width; i += nthreads) rs.hist[i] = 0;
     __syncthreads();
-    const int last = first > 0 ? first - 1 : 0;
-    for (int base = tid; base < first; base += nthreads * kUnroll) {
+    for (int it = 0; it < rounds; ++it) {
+      const int base = it * stride + tid;
       int v[kUnroll];
+      if (it == 0 && c0 == 0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int p = base + u * nthreads;
-        v[u] = idx[p < last ? p : last];
+        for (int u = 0; u < kUnroll; ++u) v[u] = v0[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int p = base + u * nthreads;
+          v[u] = idx[p < last ? p : last];
+        }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -109,15 +146,25 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
         if (p < first && rel < (unsigned)width) atomicAdd(&rs.hist[rel], 1);
       }
     }
-    if (c0 == 0) overlap();
+    if (c0 == 0) {
+      if (tid < n) {
+        rs.expert[tid] = mine;
+        rs.slot[tid] = -1;
+      }
+      overlap();
+    }
     __syncthreads();
+    if (c0 == 0) ready();
     if (n <= kWave) {
       // one chunk: rank = earlier lanes with the same expert (register walk)
       if (tid < kWave) {
         const unsigned rel = (unsigned)mine - (unsigned)c0;
         const bool here = tid < n && rel < (unsigned)width;
         int rank = 0;
-        for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
+        if (n > 3 && n <= 16)  // uniform
+          rank = same_below_in_row<1>(mine);
+        else
+          for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
         if (here) {
           const int s = rs.hist[rel] + rank;
           rs.slot[tid] = s < max_tokens ? s : -1;
