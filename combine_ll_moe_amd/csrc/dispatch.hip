@@ -86,69 +86,129 @@ __device__ __forceinline__ uint32_t e4m3_code4(float p0, float p1, float p2, flo
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest bf16 magnitude among the 8 elements of a chunk, as its 15-bit
+// pattern: magnitudes of numbers order like their bit patterns, and every
+// NaN pattern (above 0x7F80, the infinity) is larger than all of them.
+__device__ __forceinline__ uint32_t max_mag_bits(const u32x4 raw) {
+  const u16x2 a = __builtin_bit_cast(u16x2, raw.x & 0x7FFF7FFFu);
+  const u16x2 b = __builtin_bit_cast(u16x2, raw.y & 0x7FFF7FFFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, raw.z & 0x7FFF7FFFu);
+  const u16x2 d = __builtin_bit_cast(u16x2, raw.w & 0x7FFF7FFFu);
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                            __builtin_elementwise_max(c, d));
+  return (uint32_t)(m.x > m.y ? m.x : m.y);
+}
+
+// The same with NaN elements left out (0 when all eight are NaN).
+__device__ __forceinline__ uint32_t max_mag_bits_no_nan(const u32x4 raw) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t v = (w[k >> 1] >> (16 * (k & 1))) & 0x7FFFu;
+    m = v <= 0x7F80u && v > m ? v : m;
+  }
+  return m;
+}
+
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float a) {
-  const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t a) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, CTRL, 0xF, 0xF, false);
   return o > a ? o : a;
 }
 
-// Eight elements (unit u) of the fp8 message; the 16 lanes of a block
-// reduce amax together.
-__device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, const u32x4 raw) {
-  float f[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-  float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float a = __builtin_fabsf(f[j]);
-    amax = a > amax ? a : amax;
-  }
-  // max over the 16 lanes of the block by DPP within a row of 16 lanes:
-  // swap pairs, swap halves of quads, mirror halves of the row, mirror the
-  // row; every lane ends with the block's maximum (NaN never wins a compare)
-  amax = dpp_max<0xB1>(amax);   // quad_perm [1,0,3,2]
-  amax = dpp_max<0x4E>(amax);   // quad_perm [2,3,0,1]
-  amax = dpp_max<0x141>(amax);  // row_half_mirror
-  amax = dpp_max<0x140>(amax);  // row_mirror
-  float inv = 0.0f, scale = 0.0f;
-  if (amax > 0.0f) {
-    inv = 448.0f / amax;
-    scale = amax / 448.0f;
-  }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
+}
+
+// Codes and scale of unit u (eight elements) of the fp8 message, given its
+// block's inv and scale.
+__device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, const u32x4 raw,
+                                              float inv, float scale) {
+  const float f[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                      bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
   const uint32_t lo = e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
   const uint32_t hi = e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
   *reinterpret_cast<uint2*>(msg + 4 + 8 * u) = make_uint2(lo, hi);
   if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = scale;
 }
 
+// Four rounds of units, u0 + s * blockDim for s = 0..3 (all threads call
+// it; units past the end are computed and not stored). A 128-element block
+// is 16 consecutive lanes, one DPP row; the row reduces amax with four DPP
+// steps (swap pairs, swap halves of quads, mirror halves of the row, mirror
+// the row). The two divisions are then made once per lane instead of once
+// per round: lane j of every quad divides for round j, and round s takes its
+// block's inv and scale from lane s of the quad (DPP quad_perm [s,s,s,s]).
+// Every lane of a row holds the same amax, so each quad has all four.
+__device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0,
+                                                const u32x4 (&raw)[4]) {
+  const int units = hidden / 8;
+  const int B = blockDim.x;
+  uint32_t m[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) m[s] = max_mag_bits(raw[s]);
+  const uint32_t mm = (m[0] > m[1] ? m[0] : m[1]) > (m[2] > m[3] ? m[2] : m[3])
+                          ? (m[0] > m[1] ? m[0] : m[1])
+                          : (m[2] > m[3] ? m[2] : m[3]);
+  if (__builtin_expect(__ballot(mm > 0x7F80u) != 0, 0)) {  // a NaN in the wave: rare
+#pragma unroll
+    for (int s = 0; s < 4; ++s) m[s] = max_mag_bits_no_nan(raw[s]);
+  }
+  float amax[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t v = m[s];
+    v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = dpp_umax<0x141>(v);  // row_half_mirror
+    v = dpp_umax<0x140>(v);  // row_mirror
+    amax[s] = __uint_as_float(v << 16);
+  }
+  const int j = threadIdx.x & 3;
+  const float a = j == 0 ? amax[0] : j == 1 ? amax[1] : j == 2 ? amax[2] : amax[3];
+  float inv = 0.0f, scale = 0.0f;
+  if (a > 0.0f) {
+    inv = 448.0f / a;
+    scale = a / 448.0f;
+  }
+  const float inv_s[4] = {dpp_f32<0x00>(inv), dpp_f32<0x55>(inv), dpp_f32<0xAA>(inv),
+                          dpp_f32<0xFF>(inv)};
+  const float scale_s[4] = {dpp_f32<0x00>(scale), dpp_f32<0x55>(scale), dpp_f32<0xAA>(scale),
+                            dpp_f32<0xFF>(scale)};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int u = u0 + s * B;
+    if (u < units) quantize_unit(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
+  }
+}
+
 // fp8 message body: per 128-element block, amax over the block (NaN
 // ignored), inv = 448 / amax and scale = amax / 448 (correctly rounded fp32
 // divisions; both 0 when amax is 0), codes e4m3(x * inv), scales after the
-// codes. Each thread takes 8 elements; a block is 16 consecutive lanes, and
-// every lane of a 16-lane group is active together (hidden % 128 == 0 and
-// the block size is a multiple of 64). r holds the first round's loads.
+// codes. Each thread takes 8 elements per round, four rounds at a time;
+// every thread runs every round (hidden % 128 == 0 and the block size is a
+// multiple of 64, so a 16-lane row is wholly inside or outside the row of
+// x). r holds the first four rounds' loads.
 template <int NSTAGE>
 __device__ __forceinline__ void stage_fp8(uint8_t* msg, const u32x4* __restrict__ xr, int hidden,
                                           const u32x4 (&r)[NSTAGE]) {
+  static_assert(NSTAGE == 4, "one DPP quad lane per round");
   const int units = hidden / 8;
   const int B = blockDim.x;
-#pragma unroll
-  for (int s = 0; s < NSTAGE; ++s) {
-    const int u = threadIdx.x + s * B;
-    if (u < units) quantize_unit(msg, hidden, u, r[s]);
-  }
-  for (int u0 = threadIdx.x + NSTAGE * B; u0 < units; u0 += NSTAGE * B) {
+  quantize_rounds(msg, hidden, threadIdx.x, r);
+  for (int base = NSTAGE * B; base < units; base += NSTAGE * B) {  // uniform
+    const int u0 = base + threadIdx.x;
     u32x4 q[NSTAGE];
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s) {
       const int u = u0 + s * B;
       q[s] = xr[u < units ? u : units - 1];
     }
-#pragma unroll
-    for (int s = 0; s < NSTAGE; ++s) {
-      const int u = u0 + s * B;
-      if (u < units) quantize_unit(msg, hidden, u, q[s]);
-    }
+    quantize_rounds(msg, hidden, u0, q);
   }
 }
 

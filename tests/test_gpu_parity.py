@@ -142,6 +142,39 @@ def test_fp8_special_blocks():
         _run_step(st, q, x, idx, wt, y)
 
 
+def test_fp8_special_blocks_in_every_round():
+    """hidden = 9216: 1152 eight-element units, so a 256-thread workgroup
+    quantizes four rounds (blocks 0-15, 16-31, 32-47, 48-63) and then a
+    second batch (blocks 64-71). Special blocks sit in each of them."""
+    w = W.Workload("fp8r", 16, 9216, 16, 4, W.FP8_E4M3, "uniform", seed=5)
+    x = W.tokens(w)
+
+    def blk(t, b):
+        return x[t, 128 * b:128 * (b + 1)]
+
+    blk(0, 20)[:] = 0                                   # round 1: amax 0
+    blk(0, 40)[17] = 0x7FC0                             # round 2: a NaN
+    blk(0, 50)[3] = 0x7F80                              # round 3: +inf
+    blk(0, 66)[100] = 0xFFC1                            # second batch: negative NaN
+    blk(1, 33)[:] = np.arange(1, 129, dtype=np.uint16)  # round 2: subnormals
+    blk(1, 49)[:] = 0x0001                              # round 3: inv overflows
+    blk(1, 49)[5] = 0                                   #   with a zero: 0 * inf
+    blk(1, 70)[:] = 0x8000                              # second batch: all -0
+    for b in range(72):                                 # every block holds a NaN
+        blk(2, b)[(7 * b) % 128] = 0x7FC0
+    blk(3, 17)[:] = 0x7FC0                              # round 1: all NaN
+    blk(3, 63)[:] = 0xFF80                              # round 3: all -inf
+    for k, b in enumerate([0, 16, 32, 48, 64]):         # amax 448 * 2^k in each round
+        v = np.linspace(-1.0, 1.0, 128).astype(np.float32) * np.float32(448.0 * 2.0 ** (k - 2))
+        blk(4, b)[:] = W.f32_to_bf16_bits(v)
+    idx = W.routing(w)
+    wt = W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
 def test_dispatch_accumulates_when_set_not_cleaned():
     """dispatch(q) adds to set q's words; without a launch of the other
     parity in between they are not cleaned, on both sides alike."""
