@@ -103,6 +103,10 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   p.msg_bytes = (uint32_t)L.dispatch_msg;
   p.msg_stride = ((uint32_t)kMsgLdsOffset + p.msg_bytes + 15u) & ~15u;
   p.nbuf = 2 * p.msg_stride <= kDispatchLdsBudget ? 2 : 1;
+  // Large dispatches write mostly to HBM, where whole-line stores pay off;
+  // smaller ones stay in L2 and MALL, where the plain mapping is a little
+  // faster (3% at 16 MB, 24% the other way at 132 MB).
+  p.line_align = (uint64_t)num_tokens * (uint64_t)(topk + 1) * L.dispatch_msg >= kStreamRowsBytes;
   return from_hip(launch_dispatch(p, dtype, stream));
 }
 

@@ -24,6 +24,7 @@ struct DispatchParams {
   uint32_t msg_bytes;              // md
   uint32_t msg_stride;             // bytes of one LDS message buffer
   int nbuf;                        // LDS message buffers (2: double-buffered)
+  int line_align;                  // deal store chunks to lanes by whole cache lines
 };
 
 struct CombineParams {

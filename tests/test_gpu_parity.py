@@ -105,6 +105,26 @@ def test_shapes_and_base_phases(shape, pad):
         _run_step(st, q, x, idx, wt, y)
 
 
+@pytest.mark.parametrize("shape", [
+    (1024, 1024, 4104, 64, 8, W.BF16, "uniform"),
+    (1000, 1024, 4104, 64, 8, W.BF16, "hotset"),
+    (2048, 2048, 7168, 32, 8, W.FP8_E4M3, "uniform"),
+])
+def test_large_dispatch_whole_line_stores(shape):
+    """Dispatches that write 64 MiB or more deal store chunks to lanes by
+    whole 128-byte lines. Message lengths 8212 and 7396 (not multiples of
+    128) start the rows at every 4-byte phase of a line."""
+    n, cap, h, e, k, dt, routing = shape
+    w = W.Workload("lines", n, h, e, k, dt, routing, max_tokens=cap, seed=n + h)
+    md, _ = oracle.message_bytes(h, dt)
+    assert n * (k + 1) * md >= 64 << 20
+    say(f"[parity] whole-line stores: N={n} cap={cap} h={h} E={e} K={k} dtype={dt}")
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
 def test_masked_repeated_and_overflowing_picks():
     w = W.Workload("mask", 6, 64, 4, 3, W.BF16, "uniform", max_tokens=6, seed=9)
     x = W.tokens(w)
