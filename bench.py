@@ -25,6 +25,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 HOLD_CYCLES = 5_000_000
+COLD_EVICT_BYTES = 512 << 20  # twice the MI355X's 256 MB MALL
 
 
 def algorithmic_bytes(w, md: int, routed: int) -> dict:
@@ -36,7 +37,8 @@ def algorithmic_bytes(w, md: int, routed: int) -> dict:
     n, h, e, k = w.num_tokens, w.hidden, w.num_experts, w.topk
     dispatch = n * h * 2 + 4 * n * k + n * md + routed * md + 8 * e + 8 * e
     combine = 8 * n * k + routed * h * 2 + 4 * n * h + 8 * e
-    return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine}
+    return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine,
+            "dispatch_writes": n * md + routed * md}
 
 
 KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}
@@ -155,7 +157,9 @@ def summarize_profiles(args) -> None:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             cur.setdefault(r["Kernel_Name"], []).append(d)
     titles = ["dispatch + combine steps", "dispatch back to back (roofline timing)",
-              "combine back to back (roofline timing)"]
+              "combine back to back (roofline timing)",
+              "cold: after a 512 MiB eviction, event pairs between launches",
+              "warm, the same event pairs between launches"]
     lines += ["", "## The same launches by timed region of bench.py", "",
               "| region | kernel | calls | average us |", "|---|---|---|---|"]
     for title, seg in zip(titles, segs):
@@ -176,6 +180,34 @@ def summarize_profiles(args) -> None:
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print(out)
+
+
+def floor_probes(torch, stream, hold_stream, steps: int, write_bytes: int, move_bytes: int):
+    """Context for the roofline: torch's own kernels timed back to back the
+    way the step is: an empty launch, a fill writing as many bytes as the
+    dispatch writes, and a device copy moving as many bytes as the dispatch
+    moves (half read, half written)."""
+    dev = torch.device("cuda:0")
+    buf = torch.empty(write_bytes, dtype=torch.uint8, device=dev)
+    src = torch.empty(move_bytes // 2, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold_stream()
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) * 1e3 / steps, 3)
+
+    return {"empty_launch_us": timed(lambda: torch.cuda._sleep(0)),
+            "fill_us": timed(lambda: buf.fill_(7)), "fill_bytes": write_bytes,
+            "copy_us": timed(lambda: dst.copy_(src)), "copy_bytes": 2 * (move_bytes // 2)}
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -200,9 +232,21 @@ def cpu_baseline(w, budget_s: float) -> dict:
             break
     return {"value": round(nbytes * steps / el / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{steps} full {w.name} steps (dispatch+combine) on one host core, "
-                      f"{el * 1e6 / steps:.0f} us/step",
-            "us_per_step": round(el * 1e6 / steps, 1)}
+            "sample": f"{steps} full {w.name} steps (dispatch+combine) on one host core "
+                      f"(of {os.cpu_count()} host threads), {el * 1e6 / steps:.0f} us/step",
+            "us_per_step": round(el * 1e6 / steps, 1),
+            "host_cpu": _host_cpu(), "host_threads": os.cpu_count()}
+
+
+def _host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -216,6 +260,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--trials", type=int, default=7,
+                    help="further timed repetitions of the K steps (median and min reported)")
+    ap.add_argument("--no-floors", action="store_true",
+                    help="skip the plain-kernel context timings (empty launch, fill, copy)")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed after evicting L2 and MALL (0: skip)")
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSV files (no GPU)")
     ap.add_argument("--trace")
@@ -370,8 +420,68 @@ def main():
         graph_us = best
         print(f"[bench] graph replay: {graph_us:.2f} us/step", file=sys.stderr, flush=True)
 
+    # repeated trials of the same K steps: spread of the step time
+    trials = []
+    for _ in range(args.trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold_stream()
+        a.record(stream)
+        for s in range(args.steps):
+            dispatch(s)
+            combine(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        trials.append(a.elapsed_time(b) * 1e3 / args.steps)
+
+    # cold steps: the decode working set fits in the 256 MB MALL, so back to
+    # back the step runs from cache; here a 512 MiB write evicts L2 and MALL
+    # before every step, and event pairs time each launch. The same event
+    # pairs without the eviction give the warm figure of this method (event
+    # pairs add a little to each launch, so compare the two with each other).
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device=dev)
+
+        def per_launch(evict):
+            # every step queued behind the stream hold, so the GPU runs
+            # eviction, events and launches back to back, without host gaps
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.cold_steps)]
+            torch.cuda.synchronize()
+            hold_stream()
+            for s in range(args.cold_steps):
+                if evict:
+                    scratch.fill_(s & 0xFF)
+                ev[s][0].record(stream)
+                dispatch(s)
+                ev[s][1].record(stream)
+                combine(s)
+                ev[s][2].record(stream)
+            torch.cuda.synchronize()
+            ds = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+            cs = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+            return float(np.median(ds)), float(np.median(cs))
+
+        cd, cc = per_launch(True)
+        wd, wc = per_launch(False)
+        cold = {"evict_bytes": COLD_EVICT_BYTES, "steps": args.cold_steps,
+                "us_per_step": round(cd + cc, 3), "dispatch_us": round(cd, 3),
+                "combine_us": round(cc, 3),
+                "fraction_of_hbm_peak": None,
+                "warm_same_method": {"us_per_step": round(wd + wc, 3),
+                                     "dispatch_us": round(wd, 3), "combine_us": round(wc, 3)}}
+        print(f"[bench] cold (after a {COLD_EVICT_BYTES >> 20} MiB eviction): dispatch {cd:.2f} us, "
+              f"combine {cc:.2f} us; warm with the same event pairs: {wd:.2f} / {wc:.2f} us",
+              file=sys.stderr, flush=True)
+
     ab = algorithmic_bytes(w, md, routed[0])
+    floors = None if args.no_floors else floor_probes(torch, stream, hold_stream, args.steps,
+                                                      ab["dispatch_writes"], ab["dispatch"])
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    if cold is not None:
+        cold["fraction_of_hbm_peak"] = round(
+            ab["total"] / (cold["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     dom = "dispatch" if d_us >= c_us else "combine"
     dom_us = d_us if dom == "dispatch" else c_us
     achieved = ab[dom] / (dom_us * 1e-6) / 1e9
@@ -398,6 +508,11 @@ def main():
         "fraction_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernels_us": {"dispatch": round(d_us, 3), "combine": round(c_us, 3)},
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
+        "step_trials_us": {"n": len(trials),
+                           "median": round(float(np.median(trials)), 3) if trials else None,
+                           "min": round(min(trials), 3) if trials else None},
+        "cold": cold,
+        "floors": floors,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
