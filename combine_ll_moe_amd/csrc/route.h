@@ -13,7 +13,7 @@
 // workspace, no second launch; the table is a few tens of KiB and stays in
 // L2):
 //   slot(j) = (entries before the tile naming e)      an LDS histogram
-//           + (tile entries before j naming e)        a short LDS loop
+//           + (tile entries before j naming e)        a rank in registers
 // The histogram covers kHistExperts experts per pass; more experts take
 // more passes over the earlier entries. Loads are unconditional (indices
 // clamped into the table, clamped lanes masked afterwards), so the compiler
@@ -29,7 +29,7 @@ namespace llmoe {
 
 constexpr int kWave = 64;
 constexpr int kHistExperts = 4096;
-constexpr int kMaxTileEntries = 256;  // tokens per tile * topk
+constexpr int kMaxTileEntries = kWave;  // tokens per tile * topk: one wavefront's lanes
 
 struct RouteShared {
   int expert[kMaxTileEntries];  // idx of the tile's entries, tile order
@@ -90,10 +90,9 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 //
 // Slots within the tile: an entry's slot is the histogram count of its
 // expert plus its rank among the tile's earlier entries naming the same
-// expert. Up to 16 entries (one DPP row) the rank is 15 row shifts and
-// compares, with no dependent loop; up to 64 it is a register walk in
-// wavefront 0 (also for 1-3 entries, where the walk is shorter); beyond,
-// wavefront 0 walks 64 entries at a time, keeping running counts in LDS.
+// expert. The tile's entries sit in wavefront 0's lanes. For 4-16 entries
+// (one DPP row) the rank is 15 row shifts and compares, with no dependent
+// loop; otherwise a register walk over the earlier lanes (shorter for 1-3).
 template <typename Issue = NoOverlap, typename Overlap = NoOverlap, typename Ready = NoOverlap>
 __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
@@ -155,42 +154,18 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
     }
     __syncthreads();
     if (c0 == 0) ready();
-    if (n <= kWave) {
-      // one chunk: rank = earlier lanes with the same expert (register walk)
-      if (tid < kWave) {
-        const unsigned rel = (unsigned)mine - (unsigned)c0;
-        const bool here = tid < n && rel < (unsigned)width;
-        int rank = 0;
-        if (n > 3 && n <= 16)  // uniform
-          rank = same_below_in_row<1>(mine);
-        else
-          for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
-        if (here) {
-          const int s = rs.hist[rel] + rank;
-          rs.slot[tid] = s < max_tokens ? s : -1;
-        }
-      }
-    } else if (tid < kWave) {
-      // 64 entries at a time, in order: the running count of each expert is
-      // the histogram plus the chunks already walked
-      for (int j0 = 0; j0 < n; j0 += kWave) {  // uniform in wavefront 0
-        const int j = j0 + tid;
-        const int e = j < n ? rs.expert[j] : -1;
-        const unsigned rel = (unsigned)e - (unsigned)c0;
-        const bool here = j < n && rel < (unsigned)width;
-        const int base_count = here ? rs.hist[rel] : 0;
-        int rank = 0, group = 0;
-        for_each_distinct(here ? (int)rel : -1, [&](int v, uint64_t same) {
-          if (here && (int)rel == v) {
-            rank = __popcll(same & lanes_below());
-            group = __popcll(same);
-          }
-        });
-        if (here) {
-          const int s = base_count + rank;
-          rs.slot[j] = s < max_tokens ? s : -1;
-          if (rank == 0) rs.hist[rel] += group;  // the lowest lane of each value
-        }
+    if (tid < kWave) {
+      // rank = earlier lanes of wavefront 0 holding the same expert
+      const unsigned rel = (unsigned)mine - (unsigned)c0;
+      const bool here = tid < n && rel < (unsigned)width;
+      int rank = 0;
+      if (n > 3 && n <= 16)  // uniform
+        rank = same_below_in_row<1>(mine);
+      else
+        for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
+      if (here) {
+        const int s = rs.hist[rel] + rank;
+        rs.slot[tid] = s < max_tokens ? s : -1;
       }
     }
     __syncthreads();

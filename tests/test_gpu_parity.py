@@ -139,6 +139,51 @@ def test_masked_repeated_and_overflowing_picks():
     assert cnt[0] == 6  # capacity reached: later picks of expert 0 dropped
 
 
+@pytest.mark.parametrize("shape", [
+    # (N, Nmax, h, E, K, dtype): messages near the 45056-byte limit leave LDS
+    # room for one message buffer; the N=1024 cases take two-token tiles
+    # (the single buffer is reused with a barrier) and whole-line stores;
+    # fp8 at h=43648 quantizes in six batches of four rounds
+    (64, 64, 22520, 16, 4, W.BF16),
+    (1024, 1024, 22520, 16, 2, W.BF16),
+    (32, 32, 43648, 8, 2, W.FP8_E4M3),
+    (1024, 1024, 43648, 8, 2, W.FP8_E4M3),
+])
+def test_largest_messages(shape):
+    n, cap, h, e, k, dt = shape
+    md, _ = oracle.message_bytes(h, dt)
+    assert 2 * (((12 + md) + 15) // 16 * 16) > 65536 - 18432 and md <= ll.MAX_MESSAGE_BYTES
+    say(f"[parity] largest messages: N={n} h={h} E={e} K={k} dtype={dt} md={md}")
+    w = W.Workload("big", n, h, e, k, dt, "uniform", max_tokens=cap, seed=h + n)
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
+@pytest.mark.parametrize("shape", [
+    # (N, E, K): one-token tiles of 8 entries (DPP-row ranks), and two-token
+    # tiles of 32 entries (the register walk); experts drawn with
+    # replacement, so tokens repeat experts, plus masked entries and
+    # experts that overflow their capacity
+    (64, 8, 8),
+    (1024, 32, 16),
+])
+def test_repeated_picks_in_every_rank_path(shape):
+    n, e, k = shape
+    w = W.Workload("rep", n, 64, e, k, W.BF16, "uniform", seed=n + k)
+    rng = np.random.default_rng(n * 31 + k)
+    idx = rng.integers(-1, e + 1, size=(n, k)).astype(np.int32)  # -1 and e are masked
+    x = W.tokens(w)
+    wt = W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    _, cnt = oracle.route(idx, e, n)
+    say(f"[parity] repeated picks: N={n} E={e} K={k}, max count {int(cnt.max())} of {n}")
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
 def test_fp8_special_blocks():
     w = W.Workload("fp8s", 8, 1024, 8, 2, W.FP8_E4M3, "uniform", seed=4)
     x = W.tokens(w)
