@@ -21,6 +21,9 @@ namespace {
 constexpr int kTargetBlocks = 512;
 constexpr int kMaxTileTokens = 2;
 constexpr uint64_t kStreamRowsBytes = 64ull << 20;
+// LDS a dispatch workgroup may use for message buffers: 64 KiB less the
+// routing prologue's static share.
+constexpr uint32_t kDispatchLdsBudget = 65536 - (uint32_t)sizeof(RouteShared);
 
 int tile_for(int num_tokens, int per_token_blocks, int topk) {
   int tile = (int)(((int64_t)num_tokens * per_token_blocks) / kTargetBlocks);

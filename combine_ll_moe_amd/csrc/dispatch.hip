@@ -14,17 +14,17 @@
 //    computes the token's slots (route.h), then streams the message from LDS
 //    to its share of the destinations: every groups-th pick's receive row
 //    and an equal part of the send row, so that no group carries a whole
-//    extra message.
+//    extra message. The send part needs no slot and goes out while the
+//    slots are being ranked.
 //  - Message rows are 4 + 2h bytes apart, so a destination starts at any
 //    4-byte phase. Stores are aligned to the destination instead: 0-3 head
-//    dwords, then whole 16-byte global_store_dwordx4 chunks, then 0-3 tail
-//    dwords; the LDS side absorbs the phase (dword-granular LDS reads).
-//  - The (message, chunk) pairs of a workgroup are dealt to its threads as
-//    one flat sequence, so the last round of one message does not idle
-//    threads while the next message waits.
+//    dwords, then whole 16-byte chunks, then 0-3 tail dwords; the LDS side
+//    absorbs the phase (dword-granular LDS reads). Large dispatches deal the
+//    chunks to lanes by whole 128-byte cache lines (copy_message).
 //  - Messages are written with device-coherent (write-through) stores;
 //    every wave waits for its own stores, then after a workgroup barrier
-//    one lane per routed pick adds 1 to the expert's signal word with a
+//    each wavefront adds, per distinct expert among its routed picks, the
+//    number of those picks to the expert's signal word with one
 //    device-scope atomic. This is a release without an L2 write-back per
 //    workgroup (which costs tens of microseconds over a launch). The other
 //    set's signal words are zeroed by workgroup 0.
@@ -36,7 +36,6 @@
 #include "route.h"
 
 namespace llmoe {
-
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -354,11 +353,11 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   };
 
   // 1. the routing prologue; the loads of x[t0] go out with its first
-  //    loads, and message(t0) is built in LDS once they are back
+  //    loads, and message(t0) is built in LDS once they are back. The send
+  //    row needs no slot: this group's part of it goes out as soon as the
+  //    message is complete, while wavefront 0 ranks the slots.
   constexpr int kStage = 4;
   u32x4 r[kStage];
-  //    The send row needs no slot: this group's part of it goes out as soon
-  //    as the message is complete, while wavefront 0 computes the slots.
   route_tile(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
       [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },

@@ -56,9 +56,6 @@ constexpr int kCachePolicySc1 = 16;
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
 constexpr int kCombineBlock = 256;
-// LDS a dispatch workgroup may use for message buffers: 64 KiB less the
-// routing prologue's static share.
-constexpr uint32_t kDispatchLdsBudget = 65536 - 18432;
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

@@ -290,6 +290,52 @@ def test_identity_round_trip_exact():
         assert np.array_equal(o[nz].view(np.uint32), xf[nz].view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode_fp8"])
+def test_graph_capture_replays(name):
+    """Two steps (parity 0, then 1) captured into a HIP graph and replayed
+    three times, with eager kernels and synchronizations between replays:
+    every replay writes the same bytes and bits as the eager steps. The
+    two-step sequence is idempotent under the parity schedule (each
+    parity's launches zero the other set's words before it is reused)."""
+    w = W.WORKLOADS[name]
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    xd, idd, wtd, yd = to_dev(x), to_dev(idx), to_dev(wt), to_dev(y)
+    refs = []
+    for q in (0, 1):  # eager, checked against the oracle
+        st.dispatch(q, x, idx, x_dev=xd, idx_dev=idd)
+        st.check_dispatch(q, idx, restore=False)
+        out, ref = st.combine(q, y, idx, wt, y_dev=yd)
+        assert check_combine(out, ref) == 0
+        refs.append(out)
+    n, k = idx.shape
+    outs = [torch.empty((n, w.hidden), dtype=torch.float32, device=DEV) for _ in range(2)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            gs = torch.cuda.current_stream().cuda_stream
+            for q in (0, 1):
+                ll.ll_moe_dispatch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
+                                   xd, idd, gs)
+                ll.ll_moe_combine(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
+                                  yd, idd, wtd, outs[q], gs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:  # eager work between replays
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for q in (0, 1):
+            got = outs[q].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), refs[q].view(np.uint32)), (r, q)
+            st.check_dispatch(q, idx, restore=False)
+        say(f"[graph] {name} replay {r} ok")
+
+
 def _all_rounding_inputs():
     top = np.arange(1 << 16, dtype=np.uint32) << 16
     lows = [0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xFEDC]
