@@ -514,3 +514,30 @@ def test_sequence_check_catches_a_missing_clean():
     x, idx = W.tokens(w), W.routing(w)
     sched = [("d", 0), ("c", 0), ("d", 0), ("c", 0)]
     assert _sequence_violations(sched, w, x, idx) > 0
+
+
+ALG_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "algorithmic_bytes.txt")
+
+
+def _alg_rows():
+    rows = []
+    for line in open(ALG_GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            name, *nums = line.split()
+            rows.append((name, *map(int, nums)))
+    return rows
+
+
+@pytest.mark.parametrize("row", _alg_rows(), ids=lambda r: r[0])
+def test_algorithmic_bytes_match_hand_evaluation(row):
+    """The roofline's byte accounting (bench.algorithmic_bytes) against the
+    hand-evaluated table; every seeded workload routes all N*K picks."""
+    import bench
+    name, n, h, e, k, dt, md, routed, disp, comb = row
+    w = W.WORKLOADS[name]
+    assert (w.num_tokens, w.hidden, w.num_experts, w.topk, w.dtype) == (n, h, e, k, dt)
+    assert oracle.message_bytes(h, dt)[0] == md
+    _, cnt = oracle.route(W.routing(w), e, w.capacity)
+    assert int(cnt.sum()) == routed == n * k
+    ab = bench.algorithmic_bytes(w, md, routed)
+    assert (ab["dispatch"], ab["combine"], ab["total"]) == (disp, comb, disp + comb)
