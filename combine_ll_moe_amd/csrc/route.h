@@ -105,7 +105,9 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
   const int n = (t1 - t0) * topk;      // the tile's entries: [first, first + n)
   constexpr int kUnroll = 8;
   const int stride = nthreads * kUnroll;
-  const int rounds = (first + stride - 1) / stride;  // uniform
+  // at least one round: the first round's loads are then consumed on every
+  // path, so nothing later has to wait for them behind its own stores
+  const int rounds = first > stride ? (first + stride - 1) / stride : 1;  // uniform
   const int last = first > 0 ? first - 1 : 0;
 
   // loads of the first round and of the tile's own entries (threads j < n;
@@ -121,7 +123,8 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
   issue();
   const int mine = tid < n ? own : -1;
 
-  for (int c0 = 0; c0 < num_experts; c0 += kHistExperts) {  // uniform
+  int c0 = 0;
+  do {  // passes of kHistExperts experts; num_experts >= 1, uniform
     const int width = num_experts - c0 < kHistExperts ? num_experts - c0 : kHistExperts;
     for (int i = tid; i < width; i += nthreads) rs.hist[i] = 0;
     __syncthreads();
@@ -169,7 +172,8 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
       }
     }
     __syncthreads();
-  }
+    c0 += kHistExperts;
+  } while (c0 < num_experts);
 }
 
 }  // namespace llmoe
