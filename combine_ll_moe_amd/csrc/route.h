@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "layout.h"
 
 namespace llmoe {
@@ -123,15 +125,21 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
   issue();
   const int mine = tid < n ? own : -1;
 
-  int c0 = 0;
-  do {  // passes of kHistExperts experts; num_experts >= 1, uniform
+  // One histogram pass over experts [c0, c0 + width). The first pass is a
+  // separate instance (first_pass is a compile-time flag) that also runs
+  // the callbacks and ranks the tile, so that they run on every path
+  // through it: no load they consume can look in flight afterwards, which
+  // would make a later wait cover the stores issued in between.
+  int rank = 0;  // wavefront 0: earlier lanes holding the same expert
+  auto pass = [&](int c0, auto first_pass) {
+    constexpr bool kFirst = decltype(first_pass)::value;
     const int width = num_experts - c0 < kHistExperts ? num_experts - c0 : kHistExperts;
     for (int i = tid; i < width; i += nthreads) rs.hist[i] = 0;
     __syncthreads();
     for (int it = 0; it < rounds; ++it) {
       const int base = it * stride + tid;
       int v[kUnroll];
-      if (it == 0 && c0 == 0) {
+      if (kFirst && it == 0) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) v[u] = v0[u];
       } else {
@@ -148,7 +156,7 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
         if (p < first && rel < (unsigned)width) atomicAdd(&rs.hist[rel], 1);
       }
     }
-    if (c0 == 0) {
+    if constexpr (kFirst) {
       if (tid < n) {
         rs.expert[tid] = mine;
         rs.slot[tid] = -1;
@@ -156,24 +164,28 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
       overlap();
     }
     __syncthreads();
-    if (c0 == 0) ready();
+    if constexpr (kFirst) {
+      ready();
+      if (tid < kWave) {
+        if (n > 3 && n <= 16)  // uniform
+          rank = same_below_in_row<1>(mine);
+        else
+          for (int j = 0; j < n; ++j)
+            rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
+      }
+    }
     if (tid < kWave) {
-      // rank = earlier lanes of wavefront 0 holding the same expert
       const unsigned rel = (unsigned)mine - (unsigned)c0;
-      const bool here = tid < n && rel < (unsigned)width;
-      int rank = 0;
-      if (n > 3 && n <= 16)  // uniform
-        rank = same_below_in_row<1>(mine);
-      else
-        for (int j = 0; j < n; ++j) rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
-      if (here) {
+      if (tid < n && rel < (unsigned)width) {
         const int s = rs.hist[rel] + rank;
         rs.slot[tid] = s < max_tokens ? s : -1;
       }
     }
     __syncthreads();
-    c0 += kHistExperts;
-  } while (c0 < num_experts);
+  };
+  pass(0, std::true_type{});
+  for (int c0 = kHistExperts; c0 < num_experts; c0 += kHistExperts)  // uniform
+    pass(c0, std::false_type{});
 }
 
 }  // namespace llmoe
