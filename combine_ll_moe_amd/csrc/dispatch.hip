@@ -123,14 +123,32 @@ __device__ __forceinline__ float dpp_f32(float a) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
 }
 
+// The same conversion without the clamp and the NaN patch, for inputs known
+// to be numbers of magnitude below 464: v_cvt_pk_fp8_f32 rounds to nearest
+// even and overflows only past 464, so it gives +-448 for everything in
+// [448, 464] exactly as the clamped form does.
+__device__ __forceinline__ uint32_t e4m3_code4_in_range(float p0, float p1, float p2, float p3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+  return (uint32_t)w;
+}
+
 // Codes and scale of unit u (eight elements) of the fp8 message, given its
-// block's inv and scale.
+// block's inv and scale. IN_RANGE: the products are known to be numbers
+// below 464 in magnitude (see quantize_rounds).
+template <bool IN_RANGE>
 __device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, const u32x4 raw,
                                               float inv, float scale) {
   const float f[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-  const uint32_t lo = e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-  const uint32_t hi = e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+  uint32_t lo, hi;
+  if constexpr (IN_RANGE) {
+    lo = e4m3_code4_in_range(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    hi = e4m3_code4_in_range(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+  } else {
+    lo = e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    hi = e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+  }
   *reinterpret_cast<uint2*>(msg + 4 + 8 * u) = make_uint2(lo, hi);
   if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = scale;
 }
@@ -178,10 +196,25 @@ __device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0
                           dpp_f32<0xFF>(inv)};
   const float scale_s[4] = {dpp_f32<0x00>(scale), dpp_f32<0x55>(scale), dpp_f32<0xAA>(scale),
                             dpp_f32<0xFF>(scale)};
+  // A block with a finite amax, a finite inv and no NaN in this lane gives
+  // products of magnitude at most 448 * (1 + 2^-23): every |x| <= amax and
+  // inv is 448 / amax rounded once. Such waves skip the clamp and the NaN
+  // patch; a wave with any other block keeps them.
+  bool special = mm > 0x7F80u;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int u = u0 + s * B;
-    if (u < units) quantize_unit(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
+  for (int s = 0; s < 4; ++s) special = special || amax[s] == __builtin_inff() || inv_s[s] == __builtin_inff();
+  if (__builtin_expect(__ballot(special) == 0, 1)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int u = u0 + s * B;
+      if (u < units) quantize_unit<true>(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int u = u0 + s * B;
+      if (u < units) quantize_unit<false>(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
+    }
   }
 }
 
