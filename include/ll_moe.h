@@ -48,6 +48,8 @@
  * signal words of set q, which must be zero when it starts. Step s of a
  * decode loop runs dispatch(s & 1) then combine(s & 1). After allocating a
  * layout, clean both sets once (ll_moe_clean_signals with q = 0 and 1).
+ * A signal word counts at most 2^32 - 1 messages between cleans (the
+ * dispatch adds to its low 32 bits; one dispatch adds fewer than 2^31).
  */
 #ifndef LL_MOE_H_
 #define LL_MOE_H_
