@@ -41,6 +41,8 @@ def lib():
         L.oracle_dispatch.argtypes = [vp, i, i, i, i, i, i, i, vp, vp]
         L.oracle_combine.argtypes = [vp, i, i, i, i, i, i, i, vp, vp, vp, vp]
         L.oracle_clean.argtypes = [vp, i, i, i, i, i]
+        L.oracle_combine_send.argtypes = [vp, i, i, i, i, i, vp]
+        L.oracle_combine_recv.argtypes = [vp, i, i, i, i, i, i, i, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -134,6 +136,38 @@ def combine(image, max_tokens, hidden, num_experts, dtype, parity, expert_out, i
                               parity, _ptr(y), _ptr(idx), _ptr(w), _ptr(out))
     if rc != 0:
         raise ValueError("oracle combine rejected its arguments")
+    return out
+
+
+class FlagNotRaised(RuntimeError):
+    """The two-phase combine's receiver needs a flag the expert side has not
+    raised (the GPU reports this in its refusal word)."""
+
+
+def combine_send(image, max_tokens, hidden, num_experts, dtype, parity, expert_out):
+    """Two-phase combine, expert side: stage the outputs per (expert, token)
+    and raise the flags (high halves of set `parity`'s signal words)."""
+    y = np.ascontiguousarray(expert_out, dtype=np.uint16)
+    assert y.shape == (num_experts * max_tokens, hidden)
+    rc = lib().oracle_combine_send(_ptr(image), max_tokens, hidden, num_experts, dtype, parity,
+                                   _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle combine_send rejected its arguments or the image")
+
+
+def combine_recv(image, max_tokens, hidden, num_experts, dtype, parity, idx, weights):
+    """Two-phase combine, token side: the fma chain over the staged rows."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    n, k = idx.shape
+    assert w.shape == (n, k)
+    out = np.empty((n, hidden), dtype=np.float32)
+    rc = lib().oracle_combine_recv(_ptr(image), max_tokens, n, hidden, num_experts, k, dtype,
+                                   parity, _ptr(idx), _ptr(w), _ptr(out))
+    if rc == -2:
+        raise FlagNotRaised("a routed expert's flag is not raised")
+    if rc != 0:
+        raise ValueError("oracle combine_recv rejected its arguments")
     return out
 
 

@@ -390,6 +390,104 @@ int oracle_combine(uint8_t* image, int max_tokens, int num_tokens, int hidden,
 }
 
 /* ---------------------------------------------------------------------------
+ * Two-phase combine with parity q: the combine as a put of the expert
+ * outputs plus a flag hand-off, on a host image of the layout after
+ * dispatch(q). The pages give the buffers and the put / signal / wait
+ * contract, not this protocol; the readings taken:
+ *  - a combine message is int32 t followed by the bf16 output row
+ *    ([rocSHMEM LL_MoE_Buffers.hpp], "Message sizes", the combine message),
+ *    mc = 4 + 2h bytes;
+ *  - the expert side stages expert e's message for token t in set q's
+ *    combine send buffer at row e * max_tokens + t. The pointer table makes
+ *    that buffer the dispatch send buffer, whose rows are spent once the
+ *    dispatch is done; the combine receive buffer of set q is the dispatch
+ *    receive buffer, whose rows this phase still reads. On one device the
+ *    receiver reads the staged rows where they are: the put is the
+ *    identity;
+ *  - expert e's flag is set q's signal word e (clean_meta(): the dispatch
+ *    count words and the combine flag words are one array). The expert side
+ *    adds the number of rows it delivered to the word's high 32 bits, after
+ *    the rows ([mscclpp.h]: data first, then the signal); the receiver takes
+ *    expert e's rows once the high half equals the low half, the dispatch
+ *    count;
+ *  - a token names an expert at most once (the staging row is per expert
+ *    and token).
+ * Each launch zeroes the other set's signal words, as every launch of
+ * parity q does.
+ * ------------------------------------------------------------------------- */
+
+/* Expert side: for every expert e and slot j below its count (the low half
+ * of signal word e), t = the header of receive row e * max_tokens + j, and
+ * staging row e * max_tokens + t = message(t, expert_out row
+ * e * max_tokens + j); then signal word e += count << 32. */
+int oracle_combine_send(uint8_t* image, int max_tokens, int hidden, int num_experts,
+                        int dtype, int parity, const uint16_t* expert_out) {
+  uint64_t lay[7], md, mc;
+  if (check_call(max_tokens, 0, hidden, num_experts, 1, dtype, parity, lay) != 0)
+    return -1;
+  oracle_message_bytes(hidden, dtype, &md, &mc);
+  uint8_t* stage = image + lay[1 + parity];
+  const uint8_t* recv = image + lay[3 + parity];
+  uint8_t* sig = image + lay[5 + parity];
+  uint8_t* sig_other = image + lay[5 + (parity ^ 1)];
+  for (int e = 0; e < num_experts; ++e) put_i64(sig_other + 8 * (uint64_t)e, 0);
+  for (int e = 0; e < num_experts; ++e) {
+    uint8_t* w = sig + 8 * (uint64_t)e;
+    int64_t word = get_i64(w);
+    int64_t count = word & 0xFFFFFFFF;
+    if (count > max_tokens) return -1;
+    for (int64_t j = 0; j < count; ++j) {
+      uint64_t src = (uint64_t)e * (uint64_t)max_tokens + (uint64_t)j;
+      int32_t t;
+      memcpy(&t, recv + src * md, 4);
+      if (t < 0 || t >= max_tokens) return -1;
+      uint8_t* dst = stage + ((uint64_t)e * (uint64_t)max_tokens + (uint64_t)t) * mc;
+      memcpy(dst, &t, 4);
+      memcpy(dst + 4, expert_out + src * (uint64_t)hidden, 2 * (uint64_t)hidden);
+    }
+    put_i64(w, word + (int64_t)((uint64_t)count << 32));
+  }
+  return 0;
+}
+
+/* Token side: every routed pick of token t needs expert e's flag (high half
+ * of signal word e equal to its low half); then
+ *     out[t, c] = fma chain in ascending k, from +0.0f, of
+ *                 w[t, k] * f32(staging row e * max_tokens + t, column c).
+ * Returns -2 if a needed flag is not raised (the GPU side reports that in its
+ * refusal word instead of waiting forever). */
+int oracle_combine_recv(uint8_t* image, int max_tokens, int num_tokens, int hidden,
+                        int num_experts, int topk, int dtype, int parity,
+                        const int32_t* idx, const float* weights, float* out) {
+  uint64_t lay[7], md, mc;
+  if (check_call(max_tokens, num_tokens, hidden, num_experts, topk, dtype, parity, lay) != 0)
+    return -1;
+  oracle_message_bytes(hidden, dtype, &md, &mc);
+  const uint8_t* stage = image + lay[1 + parity];
+  const uint8_t* sig = image + lay[5 + parity];
+  uint8_t* sig_other = image + lay[5 + (parity ^ 1)];
+  for (int t = 0; t < num_tokens; ++t) {
+    float* o = out + (uint64_t)t * hidden;
+    for (int c = 0; c < hidden; ++c) o[c] = 0.0f;
+    for (int k = 0; k < topk; ++k) {
+      int32_t e = idx[(uint64_t)t * topk + k];
+      if (e < 0 || e >= num_experts) continue;
+      int64_t word = get_i64(sig + 8 * (uint64_t)e);
+      if ((word >> 32) != (word & 0xFFFFFFFF)) return -2;
+      const uint8_t* row = stage + ((uint64_t)e * (uint64_t)max_tokens + (uint64_t)t) * mc + 4;
+      float w = weights[(uint64_t)t * topk + k];
+      for (int c = 0; c < hidden; ++c) {
+        uint16_t b;
+        memcpy(&b, row + 2 * (uint64_t)c, 2);
+        o[c] = fmaf(w, bf16_to_f32(b), o[c]);
+      }
+    }
+  }
+  for (int e = 0; e < num_experts; ++e) put_i64(sig_other + 8 * (uint64_t)e, 0);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Explicit clean of set q's signal words: [rocSHMEM LL_MoE_Buffers.hpp,
  * clean_meta()] returns the signal pointer and num_sig_elems (= experts)
  * words to zero.
