@@ -156,6 +156,106 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   return from_hip(launch_combine(p, stream));
 }
 
+namespace {
+
+// Two-phase combine launch shape: the expert side spreads the received rows
+// over a fixed grid (the host does not know how many there are); the token
+// side takes the fused combine's shape.
+constexpr int kSendBlocks = 1024;
+
+int check_two_phase(const Layout& L, int hidden, int num_experts, int max_tokens, void* layout) {
+  if (hidden % 8 != 0) return LL_MOE_INVALID_ARGUMENT;
+  if (num_experts > LL_MOE_SEND_MAX_EXPERTS) return LL_MOE_INVALID_ARGUMENT;
+  if (L.combine_msg > kMaxMessageBytes) return LL_MOE_INVALID_ARGUMENT;
+  if ((int64_t)num_experts * max_tokens > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
+  if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
+  return LL_MOE_SUCCESS;
+}
+
+bool overlaps(const void* a, uint64_t a_bytes, const void* b, uint64_t b_bytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+}  // namespace
+
+extern "C" int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int num_experts,
+                                   int dtype, int parity, const void* expert_out,
+                                   hipStream_t stream) {
+  Layout L;
+  int rc = check_shape(max_tokens, 0, hidden, num_experts, 1, dtype, parity, &L);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  rc = check_two_phase(L, hidden, num_experts, max_tokens, layout);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  if (!expert_out || !aligned(expert_out, 16)) return LL_MOE_INVALID_ARGUMENT;
+  // the staging rows may not overlap the expert outputs they are copied from
+  if (overlaps(layout, L.total, expert_out, (uint64_t)num_experts * max_tokens * hidden * 2))
+    return LL_MOE_INVALID_ARGUMENT;
+
+  uint8_t* base = static_cast<uint8_t*>(layout);
+  SendParams p;
+  p.sig = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity));
+  p.sig_other = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity ^ 1));
+  p.recv = base + L.recv_off(parity);
+  p.stage = base + L.send_off(parity);
+  p.y = static_cast<const uint4*>(expert_out);
+  p.max_tokens = max_tokens;
+  p.hidden = hidden;
+  p.num_experts = num_experts;
+  p.msg_bytes = (uint32_t)L.dispatch_msg;
+  p.comb_bytes = (uint32_t)L.combine_msg;
+  // LDS: the count prefix, then one or two message buffers
+  const int rounds = num_experts <= kSendBlock ? 1 : num_experts <= 4 * kSendBlock ? 4 : 16;
+  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
+  const uint32_t stride = ((uint32_t)kMsgLdsOffset + p.comb_bytes + 15u) & ~15u;
+  p.nbuf = prefix_bytes + 2 * stride <= 65536u - 64u ? 2 : 1;
+  const int64_t most_rows = (int64_t)num_experts * max_tokens;
+  const int blocks = most_rows < kSendBlocks ? (int)most_rows : kSendBlocks;
+  return from_hip(launch_combine_send(p, blocks, stream));
+}
+
+extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden,
+                                   int num_experts, int topk, int dtype, int parity,
+                                   const int32_t* topk_idx, const float* topk_weights, float* out,
+                                   int max_spins, int32_t* refusal, hipStream_t stream) {
+  Layout L;
+  int rc = check_shape(max_tokens, num_tokens, hidden, num_experts, topk, dtype, parity, &L);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  rc = check_two_phase(L, hidden, num_experts, max_tokens, layout);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  if (max_spins < 1) return LL_MOE_INVALID_ARGUMENT;
+  if (num_tokens > 0) {
+    if (!topk_idx || !topk_weights || !out || !refusal) return LL_MOE_INVALID_ARGUMENT;
+    if (!aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+        !aligned(refusal, 4))
+      return LL_MOE_INVALID_ARGUMENT;
+    // out may not overlap the layout whose staging rows it folds
+    if (overlaps(layout, L.total, out, (uint64_t)num_tokens * hidden * 4))
+      return LL_MOE_INVALID_ARGUMENT;
+  }
+
+  uint8_t* base = static_cast<uint8_t*>(layout);
+  RecvParams p;
+  p.sig = reinterpret_cast<const unsigned long long*>(base + L.sig_off(parity));
+  p.sig_other = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity ^ 1));
+  p.stage = base + L.send_off(parity);
+  p.idx = topk_idx;
+  p.w = topk_weights;
+  p.out = reinterpret_cast<float4*>(out);
+  p.refusal = refusal;
+  p.num_tokens = num_tokens;
+  p.max_tokens = max_tokens;
+  p.hidden = hidden;
+  p.num_experts = num_experts;
+  p.topk = topk;
+  p.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
+  p.tile = tile_for(num_tokens, p.slices, topk);
+  p.comb_bytes = (uint32_t)L.combine_msg;
+  p.max_spins = max_spins;
+  p.stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
+  return from_hip(launch_combine_recv(p, stream));
+}
+
 extern "C" int ll_moe_clean_signals(void* layout, int max_tokens, int hidden, int num_experts,
                                     int dtype, int parity, hipStream_t stream) {
   Layout L;

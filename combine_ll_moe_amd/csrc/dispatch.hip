@@ -34,29 +34,9 @@
 #include "kernels.h"
 #include "layout.h"
 #include "route.h"
+#include "message.h"
 
 namespace llmoe {
-
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Message stores are buffer stores with the device-scope coherence bit
-// (sc1): they write through the XCD's L2, so they are visible to every XCD
-// once complete, and no L2 write-back is needed before the count is
-// published. The buffer descriptor covers exactly one message, so a store
-// can never leave it.
-typedef __amdgpu_buffer_rsrc_t BufRsrc;
-
-__device__ __forceinline__ BufRsrc message_rsrc(void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
-}
-__device__ __forceinline__ void store_b128(const u32x4_a4 v, BufRsrc r, uint32_t off) {
-  const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kCachePolicySc1);
-}
-__device__ __forceinline__ void store_b32(uint32_t v, BufRsrc r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCachePolicySc1);
-}
 
 // fp32 -> OCP e4m3 ("e4m3fn") codes, round to nearest even, saturating to
 // +-448; the infinities saturate and every NaN gives 0x7F. Four values per
@@ -244,18 +224,6 @@ __device__ __forceinline__ void stage_fp8(uint8_t* msg, const u32x4* __restrict_
   }
 }
 
-// Row t of x (first kStage * blockDim chunks) into registers; unconditional
-// loads with the index clamped into the row.
-template <int NSTAGE>
-__device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __restrict__ xr,
-                                         int chunks) {
-#pragma unroll
-  for (int u = 0; u < NSTAGE; ++u) {
-    const int j = (int)threadIdx.x + u * (int)blockDim.x;
-    r[u] = xr[j < chunks ? j : chunks - 1];
-  }
-}
-
 // message(t) into an LDS buffer: header, then the bf16 row or its fp8 form.
 // r holds the row's first round of loads.
 template <int DT, int NSTAGE>
@@ -286,74 +254,6 @@ __device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* 
     }
   } else {
     stage_fp8<NSTAGE>(msg, xr, hidden, r);
-  }
-}
-
-// Part `part` of `parts` of one message, from LDS to its destination. The
-// destination splits into 0-3 head dwords, whole 16-byte body chunks and
-// 0-3 tail dwords; part p takes body chunks [nb * p / parts, nb * (p + 1) /
-// parts), the first part also the head and the last the tail (one thread
-// each). Body chunks go four per thread per round, with the round's LDS
-// reads issued before its stores; the stores are destination-aligned,
-// device-coherent, and confined to the message by the buffer descriptor.
-//
-// With LINE, chunks are dealt to lanes so that every 8 lanes write
-// one whole 128-byte cache line: chunk k goes to virtual index k + sh, where
-// sh is the body's 16-byte offset within its first line, and lanes of a
-// round take consecutive virtual indices from a multiple of 8. A 1 KiB wave
-// store then covers 8 whole lines instead of straddling 9; for write-through
-// stores that go to HBM this is a quarter faster. (For data the caches
-// absorb it costs a little, so the caller decides.)
-template <bool LINE>
-__device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32_t md,
-                                             uint32_t part = 0, uint32_t parts = 1) {
-  constexpr int kCopy = 4;
-  const uint32_t tid = threadIdx.x;
-  const BufRsrc rsrc = message_rsrc(d, md);
-  const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
-  const uint32_t nb = (md - head) >> 4;
-  const uint32_t body_end = head + 16u * nb;
-  const uint32_t c0 = nb * part / parts;
-  const uint32_t c1 = nb * (part + 1) / parts;
-  if (part == 0 && tid == 0)
-    for (uint32_t b = 0; b < head; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
-  if (part == parts - 1 && tid == 1)
-    for (uint32_t b = body_end; b < md; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
-  if constexpr (!LINE) {
-    for (uint32_t i0 = c0 + tid; i0 < c1; i0 += kCopy * blockDim.x) {
-      u32x4_a4 v[kCopy];
-#pragma unroll
-      for (int u = 0; u < kCopy; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
-        v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < c1 ? i : c1 - 1));
-      }
-#pragma unroll
-      for (int u = 0; u < kCopy; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
-        if (i < c1) store_b128(v[u], rsrc, head + 16u * i);
-      }
-    }
-    return;
-  }
-  if (c1 <= c0) return;
-  // virtual indices [vlo, vend) hold chunks [c0, c1); a round starts at a
-  // multiple of 8
-  const uint32_t sh = (((uint32_t)(uintptr_t)d + head) & 127u) >> 4;
-  const uint32_t vlo = c0 + sh;
-  const uint32_t vend = c1 + sh;
-  for (uint32_t v0 = (vlo & ~7u) + tid; v0 < vend; v0 += kCopy * blockDim.x) {
-    u32x4_a4 v[kCopy];
-#pragma unroll
-    for (int u = 0; u < kCopy; ++u) {
-      const uint32_t vi = v0 + u * blockDim.x;
-      const uint32_t k = vi >= vlo && vi < vend ? vi - sh : c0;
-      v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * k);
-    }
-#pragma unroll
-    for (int u = 0; u < kCopy; ++u) {
-      const uint32_t vi = v0 + u * blockDim.x;
-      if (vi >= vlo && vi < vend) store_b128(v[u], rsrc, head + 16u * (vi - sh));
-    }
   }
 }
 

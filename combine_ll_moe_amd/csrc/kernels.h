@@ -43,6 +43,46 @@ struct CombineParams {
   int stream_rows;                 // read the expert rows with non-temporal loads
 };
 
+struct SendParams {                // two-phase combine, expert side
+  unsigned long long* sig;         // signal words of set q (counts; flags in the high halves)
+  unsigned long long* sig_other;   // signal words of set 1-q (zeroed)
+  const uint8_t* recv;             // receive buffer of set q (dispatch messages)
+  uint8_t* stage;                  // combine send buffer of set q (= its send buffer)
+  const uint4* y;                  // bf16 [num_experts * max_tokens, hidden] as 16-byte chunks
+  int max_tokens;
+  int hidden;
+  int num_experts;
+  uint32_t msg_bytes;              // md: dispatch message bytes
+  uint32_t comb_bytes;             // mc: combine message bytes
+  int nbuf;                        // LDS message buffers (2: double-buffered)
+};
+
+struct RecvParams {                // two-phase combine, token side
+  const unsigned long long* sig;   // signal words of set q
+  unsigned long long* sig_other;   // signal words of set 1-q (zeroed)
+  const uint8_t* stage;            // combine send buffer of set q
+  const int32_t* idx;              // int32 [num_tokens, topk]
+  const float* w;                  // fp32 [num_tokens, topk]
+  float4* out;                     // fp32 [num_tokens, hidden]
+  int32_t* refusal;                // refusal word: set when a flag wait runs out
+  int num_tokens;
+  int max_tokens;
+  int hidden;
+  int num_experts;
+  int topk;
+  int tile;                        // consecutive tokens per workgroup
+  int slices;                      // workgroups per tile, each a contiguous run of columns
+  uint32_t comb_bytes;             // mc
+  int max_spins;                   // polls of one flag before its wait gives up
+  int stream_rows;                 // read the staging rows with non-temporal loads
+};
+
+// The two-phase combine's expert side keeps every expert's count in LDS.
+constexpr int kSendMaxExperts = 4096;
+constexpr int kSendBlock = 256;
+// Refusal code of ll_moe_combine_recv: a flag wait ran out.
+constexpr int32_t kRefusalFlagWait = 1;
+
 // LDS placement of a message: it starts at this offset of its buffer, so
 // that the payload (message byte 4) is 16-byte aligned; a buffer is
 // kMsgLdsOffset + md rounded up to 16 bytes.
@@ -59,6 +99,8 @@ constexpr int kCombineBlock = 256;
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream);
+hipError_t launch_combine_recv(const RecvParams& p, hipStream_t stream);
 hipError_t launch_clean(unsigned long long* sig, int num_experts, hipStream_t stream);
 hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, hipStream_t stream);
 

@@ -1,0 +1,353 @@
+// Two-phase combine: the expert side stages each output as a combine
+// message and raises a flag per expert; the token side waits for the flags
+// of its picks and folds the staged rows.
+//
+// What is computed (rocSHMEM example LL_MoE/LL_MoE_Buffers.hpp, struct
+// LLMoEBuffer's combine buffers and flag, aliased by LLMoEBufferLayout's
+// pointer table to the set's dispatch buffers; mscclpp.h, put-then-signal
+// above struct mscclppDevConn; memra-engine src/tp_ar.rs, a fold ordered
+// after the push and a bounded wait that leaves a refusal code):
+//   expert side: for expert e and j < count_e, with t the header of receive
+//     row e * max_tokens + j, staging row e * max_tokens + t := [int32 t |
+//     expert output row e * max_tokens + j]; then the high half of signal
+//     word e rises by the rows staged for e (count in the low half);
+//   token side: once every routed pick's flag is up (high == low), the
+//     fused combine's fma chain over the staging rows.
+//
+// Design on gfx950:
+//  - Expert side. The work is the flattened (expert, slot) order of the
+//    received messages, which only the counts describe: every workgroup
+//    loads all counts and forms their exclusive prefix in LDS, then takes a
+//    contiguous run of rows, 64 at a time. Lane l finds its row's expert by
+//    binary search in the prefix and loads the row's header; then the
+//    workgroup copies the rows one by one through LDS (the source row is
+//    16-byte aligned, the staging row starts at any 4-byte phase, and the
+//    phase is only known once the header is back: the row's loads go out
+//    together with the header load), next row's loads in flight while the
+//    current row is stored. Release as in the dispatch: device-coherent
+//    stores, each wave waits for its own, a barrier, then wave 0 adds per
+//    distinct expert the rows it staged to the flag with one device-scope
+//    atomic on the word's high half.
+//  - Token side. One workgroup per (tile of tokens, run of columns), as the
+//    fused combine, but no routing prologue: a token's staging row for pick
+//    k is e * max_tokens + t. Each wavefront polls the flags of a token's
+//    picks itself (lane k polls pick k, relaxed device-scope loads, at most
+//    max_spins rounds), then an acquire fence, then the fused combine's
+//    gather and fma chain, reading the staged payload (4 bytes past the row
+//    start, so 4-byte aligned 16-byte loads).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "message.h"
+#include "route.h"
+
+namespace llmoe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Rows at or above this many bytes go out with whole-cache-line lane
+// mapping (mostly HBM-bound writes); smaller ones stay in the caches.
+constexpr uint64_t kSendLineBytes = 64ull << 20;
+
+// Exclusive prefix of the counts (low halves of the signal words, each
+// taken as at most max_tokens) into pre[0..E], pre[E] = total rows.
+// ROUNDS * kSendBlock >= E. Thread tid loads experts tid + r * kSendBlock
+// (coalesced, all loads issued before any is used), the counts go to LDS,
+// then thread tid sums the contiguous run [tid * ROUNDS, (tid + 1) * ROUNDS)
+// and a workgroup scan of the run sums gives each run its base.
+template <int ROUNDS>
+__device__ __forceinline__ void count_prefix(const SendParams& P, uint32_t* pre,
+                                             uint32_t* wave_sum) {
+  const int tid = threadIdx.x;
+  const int E = P.num_experts;
+  uint32_t c[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int e = tid + r * kSendBlock;
+    const uint64_t w = __hip_atomic_load(P.sig + (e < E ? e : E - 1), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n = (uint32_t)w;
+    c[r] = e < E ? (n < (uint32_t)P.max_tokens ? n : (uint32_t)P.max_tokens) : 0u;
+  }
+  // the headers and expert rows written before the counts were raised are
+  // visible from here on
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) pre[tid + r * kSendBlock] = c[r];
+  __syncthreads();
+  uint32_t run[ROUNDS];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    run[i] = sum;
+    sum += pre[tid * ROUNDS + i];
+  }
+  // inclusive scan of the run sums within the wavefront, then across waves
+  const int lane = tid & (kWave - 1);
+  uint32_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_sum[tid / kWave] = incl;
+  __syncthreads();
+  uint32_t base = incl - sum;
+  for (int w = 0; w < tid / kWave; ++w) base += wave_sum[w];
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) pre[tid * ROUNDS + i] = base + run[i];
+  if (tid == kSendBlock - 1) pre[kSendBlock * ROUNDS] = base + sum;
+  __syncthreads();
+}
+
+// Expert of flattened row r: the largest e < E with pre[e] <= r (an expert
+// with no rows has pre[e] == pre[e + 1], so it is never the answer for a
+// row below pre[E]).
+__device__ __forceinline__ int expert_of_row(const uint32_t* pre, int E, uint32_t r) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool LINE>
+__device__ __forceinline__ void stage_rows(const SendParams& P, uint32_t* pre, uint8_t* lds_msg,
+                                           uint32_t msg_stride, int nbuf, uint32_t r0, uint32_t r1) {
+  constexpr int kStage = 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int E = P.num_experts;
+  const int chunks = P.hidden / 8;
+  const uint32_t mc = P.comb_bytes;
+  const u32x4* y = reinterpret_cast<const u32x4*>(P.y);
+  auto msg_buffer = [&](int i) { return lds_msg + (nbuf == 2 ? (i & 1) : 0) * msg_stride; };
+
+  for (uint32_t b0 = r0; b0 < r1; b0 += kWave) {
+    const int n = r1 - b0 < (uint32_t)kWave ? (int)(r1 - b0) : kWave;
+    // this lane's row of the batch: expert, slot and header
+    const uint32_t r = b0 + (uint32_t)(lane < n ? lane : n - 1);
+    const int e_l = expert_of_row(pre, E, r);
+    const int j_l = (int)(r - pre[e_l]);
+    const uint64_t src_l = (uint64_t)e_l * (uint64_t)P.max_tokens + (uint64_t)j_l;
+    const int t_l = *reinterpret_cast<const int32_t*>(P.recv + src_l * P.msg_bytes);
+
+    auto src_row = [&](int i) {
+      const int e = __builtin_amdgcn_readlane(e_l, i);
+      const int j = __builtin_amdgcn_readlane(j_l, i);
+      return y + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)j) * (uint64_t)chunks;
+    };
+    u32x4 v[kStage];
+    load_row<kStage>(v, src_row(0), chunks);
+    for (int i = 0; i < n; ++i) {
+      uint8_t* msg = msg_buffer(i);
+      if (nbuf == 1 && i > 0) __syncthreads();  // the single buffer is still being read
+      // message = [t | row]: the row's first kStage rounds from registers,
+      // further rounds (hidden > kStage * 8 * blockDim) straight through
+      const int t = __builtin_amdgcn_readlane(t_l, i);
+      if (tid == 0) *reinterpret_cast<int32_t*>(msg) = t;
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + u * kSendBlock;
+        if (c < chunks) *reinterpret_cast<u32x4*>(msg + 4 + 16 * c) = v[u];
+      }
+      const u32x4* src = src_row(i);
+      for (int c = tid + kStage * kSendBlock; c < chunks; c += kSendBlock)
+        *reinterpret_cast<u32x4*>(msg + 4 + 16 * c) = src[c];
+      __syncthreads();
+      if (i + 1 < n) load_row<kStage>(v, src_row(i + 1), chunks);
+      const int e = __builtin_amdgcn_readlane(e_l, i);
+      if (t >= 0 && t < P.max_tokens)
+        copy_message<LINE>(P.stage + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)t) * mc, msg, mc);
+    }
+
+    // release: this wave's stores are complete, then every wave's; wave 0
+    // adds per distinct expert the number of rows staged for it to the
+    // word's high half (little-endian: byte offset 4)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid < kWave) {
+      const int e = lane < n && t_l >= 0 && t_l < P.max_tokens ? e_l : -1;
+      int group = 0;
+      for_each_distinct(e, [&](int val, uint64_t same) {
+        if (e == val && (same & lanes_below()) == 0) group = __popcll(same);
+      });
+      if (group > 0)
+        __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + e) + 1, (unsigned int)group,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendParams P) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  __shared__ uint32_t wave_sum[kSendBlock / kWave];
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
+
+  uint32_t* pre = reinterpret_cast<uint32_t*>(lds_raw);
+  if (P.num_experts <= kSendBlock)
+    count_prefix<1>(P, pre, wave_sum);
+  else if (P.num_experts <= 4 * kSendBlock)
+    count_prefix<4>(P, pre, wave_sum);
+  else
+    count_prefix<kSendMaxExperts / kSendBlock>(P, pre, wave_sum);
+  // pre[kSendBlock * ROUNDS] is the total; rows beyond E have zero counts
+  const int rounds = P.num_experts <= kSendBlock ? 1 : P.num_experts <= 4 * kSendBlock ? 4 : 16;
+  const uint32_t rows = pre[kSendBlock * rounds];
+
+  const uint32_t r0 = (uint32_t)((uint64_t)rows * blockIdx.x / gridDim.x);
+  const uint32_t r1 = (uint32_t)((uint64_t)rows * (blockIdx.x + 1) / gridDim.x);
+  if (r0 >= r1) return;
+  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
+  uint8_t* lds_msg = lds_raw + prefix_bytes + kMsgLdsOffset;
+  const uint32_t msg_stride = ((uint32_t)kMsgLdsOffset + P.comb_bytes + 15u) & ~15u;
+  if ((uint64_t)rows * P.comb_bytes >= kSendLineBytes)
+    stage_rows<true>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
+  else
+    stage_rows<false>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
+}
+
+hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream) {
+  const int rounds = p.num_experts <= kSendBlock ? 1 : p.num_experts <= 4 * kSendBlock ? 4 : 16;
+  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
+  const uint32_t msg_stride = ((uint32_t)kMsgLdsOffset + p.comb_bytes + 15u) & ~15u;
+  const size_t lds = prefix_bytes + (size_t)p.nbuf * msg_stride;
+  combine_send_kernel<<<blocks, kSendBlock, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Token t's gather-fold over this thread's 8 columns, once the flags are
+// up. Lane k of the wavefront holds pick k's expert (e_l, or -1 when masked)
+// and weight (w_l); a masked pick borrows a routed pick's row so that the
+// loads stay unconditional, and its value is never used.
+template <int MAXK, bool STREAM>
+__device__ __forceinline__ void fold_token(const RecvParams& P, int t, int c, int e_l, float w_l) {
+  const uint8_t* stage = P.stage + 4 + 16 * (uint64_t)c;
+  uint64_t row[MAXK];
+  bool routed[MAXK];
+  float w[MAXK];
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    const int e = __builtin_amdgcn_readlane(e_l, k < P.topk ? k : 0);
+    routed[k] = k < P.topk && e >= 0;
+    row[k] = (uint64_t)(routed[k] ? e : 0) * (uint64_t)P.max_tokens + (uint64_t)t;
+    w[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), k < P.topk ? k : 0));
+  }
+  bool any = false;
+  uint64_t fallback = 0;
+#pragma unroll
+  for (int k = MAXK - 1; k >= 0; --k) {
+    fallback = routed[k] ? row[k] : fallback;
+    any = any || routed[k];
+  }
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  if (any) {
+    u32x4 v[MAXK];
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      const u32x4_a4* src =
+          reinterpret_cast<const u32x4_a4*>(stage + (routed[k] ? row[k] : fallback) * P.comb_bytes);
+      const u32x4_a4 q = STREAM ? __builtin_nontemporal_load(src) : *src;
+      v[k] = u32x4{q.x, q.y, q.z, q.w};
+    }
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float a = __builtin_fmaf(w[k], __uint_as_float(q[h] << 16), acc[2 * h]);
+        const float b = __builtin_fmaf(w[k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
+        acc[2 * h] = routed[k] ? a : acc[2 * h];
+        acc[2 * h + 1] = routed[k] ? b : acc[2 * h + 1];
+      }
+    }
+  }
+  const int chunks = P.hidden / 8;
+  f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
+  const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
+  const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
+  __builtin_nontemporal_store(lo, o);
+  __builtin_nontemporal_store(hi, o + 1);
+}
+
+template <int MAXK, bool STREAM>
+__global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvParams P) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
+
+  // workgroup -> (tile of tokens [t0, t1), run of columns sl)
+  const int tile = blockIdx.x / P.slices;
+  const int sl = blockIdx.x - tile * P.slices;
+  const int t0 = tile * P.tile;
+  if (t0 >= P.num_tokens) return;
+  const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
+  const int chunks = P.hidden / 8;
+  const int c0 = sl * (int)blockDim.x + (tid & ~(kWave - 1));  // this wavefront's first column
+  if (c0 >= chunks) return;  // the whole wavefront is past the row
+  const int c = sl * (int)blockDim.x + tid;
+  const int lane = tid & (kWave - 1);
+
+  bool refused = false;
+  for (int t = t0; t < t1; ++t) {
+    int e_l = -1;
+    float w_l = 0.0f;
+    if (lane < P.topk) {
+      const int e = P.idx[(uint64_t)t * P.topk + lane];
+      e_l = e >= 0 && e < P.num_experts ? e : -1;
+      w_l = P.w[(uint64_t)t * P.topk + lane];
+    }
+    // bounded wait for the flags of this token's routed picks
+    if (!refused) {
+      for (int spins = 1;; ++spins) {
+        bool pending = false;
+        if (e_l >= 0) {
+          const uint64_t s = __hip_atomic_load(P.sig + e_l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          pending = (uint32_t)(s >> 32) != (uint32_t)s;
+        }
+        if (__ballot(pending) == 0) break;
+        if (spins >= P.max_spins) {
+          refused = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (refused && lane == 0)
+        __hip_atomic_fetch_or(P.refusal, kRefusalFlagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (refused) continue;  // out stays unwritten from here on
+    if (c < chunks) fold_token<MAXK, STREAM>(P, t, c, e_l, w_l);
+  }
+}
+
+template <bool STREAM>
+static void launch_recv_k(const RecvParams& p, int blocks, hipStream_t stream) {
+  if (p.topk <= 2)
+    combine_recv_kernel<2, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 4)
+    combine_recv_kernel<4, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else if (p.topk <= 8)
+    combine_recv_kernel<8, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+  else
+    combine_recv_kernel<16, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+}
+
+hipError_t launch_combine_recv(const RecvParams& p, hipStream_t stream) {
+  const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
+  const int blocks = tiles * p.slices;
+  if (p.stream_rows)
+    launch_recv_k<true>(p, blocks, stream);
+  else
+    launch_recv_k<false>(p, blocks, stream);
+  return hipGetLastError();
+}
+
+}  // namespace llmoe

@@ -161,6 +161,94 @@ int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int hidden,
                    const float* topk_weights, float* out, hipStream_t stream);
 
 /*
+ * Two-phase combine: the combine as a put from the expert side followed by a
+ * wait-and-fold on the token side, the form a combine takes when expert and
+ * token live on different devices.
+ *   - rocSHMEM example "LL_MoE/LL_MoE_Buffers.hpp", struct LLMoEBuffer: the
+ *     combine send and receive buffers ([num_experts * num_tokens,
+ *     hidden + 1], bf16 payload) and the int64 combine flag per expert; the
+ *     pointer table of LLMoEBufferLayout aliases them to the dispatch buffers
+ *     of the same set, and clean_meta() treats count and flag as one array.
+ *   - mscclpp "mscclpp.h", comment above struct mscclppDevConn: the data is
+ *     put first and signalled after; the receiver reads it only after the
+ *     signal.
+ *   - memra-engine "src/tp_ar.rs": the fold of staged data is ordered after
+ *     the peer's push (memra_tp_ar_fold), and a device wait is bounded and
+ *     leaves a refusal code when it runs out (memra_tp_ar_1stage).
+ * On one GPU the put is a local copy: the combine message of token t from
+ * expert e is staged at row e * max_tokens + t of set q's combine send
+ * buffer (= its send buffer, spent once the dispatch of set q is complete),
+ * and expert e's flag is the high 32 bits of signal word e of set q. The
+ * dispatch's count sits in the low 32 bits; the flag is up once
+ * high == low. Neither call resets the flags: the next launch of parity 1-q
+ * zeroes set q, as for the counts.
+ * Both calls need hidden % 8 == 0, a combine message of at most
+ * LL_MOE_MAX_MESSAGE_BYTES (hidden <= 22520), num_experts <=
+ * LL_MOE_SEND_MAX_EXPERTS, num_experts * max_tokens < 2^31, and at most one
+ * pick per (token, expert) in the routing (two picks of one expert would
+ * share one staging row). Neither writes outside the regions it names.
+ */
+#define LL_MOE_SEND_MAX_EXPERTS 4096
+#define LL_MOE_REFUSAL_FLAG_WAIT 1
+
+/*
+ * ll_moe_combine_send — expert side: stage every received message's output
+ * and raise the flags of set `parity`.
+ *   layout:     device, as for dispatch. Read: the low halves of set q's
+ *               signal words (the dispatch counts) and the int32 headers of
+ *               set q's receive rows. Written: set q's send buffer (staging
+ *               rows only), the high halves of set q's signal words, and set
+ *               1-q's signal words (zeroed).
+ *   expert_out: device, bf16 [num_experts * max_tokens, hidden], 16-byte
+ *               aligned, in receive-slot order as for ll_moe_combine.
+ * For every expert e and j < count_e (count_e = low half of signal word e,
+ * taken as max_tokens if larger), with t = the header of receive row
+ * e * max_tokens + j: staging row e * max_tokens + t, at send_q +
+ * (e * max_tokens + t) * mc, := int32 t, then the bits of expert_out row
+ * e * max_tokens + j. Then the high half of signal word e is raised by the
+ * number of rows staged for e, with device-scope release semantics after
+ * those rows. A header outside [0, max_tokens) stages nothing, so that
+ * expert's flag never comes up.
+ * Order: after the dispatch of set q and after expert_out is written
+ * (stream order or events). expert_out may not overlap the layout.
+ * Enqueued on `stream`.
+ */
+int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int num_experts,
+                        int dtype, int parity, const void* expert_out,
+                        hipStream_t stream);
+
+/*
+ * ll_moe_combine_recv — token side: wait for the flag of every routed
+ * expert of a token, then fold the staged rows.
+ *   layout:       device, as for dispatch. Read: set q's signal words and
+ *                 staging rows. Written: set 1-q's signal words (zeroed).
+ *   topk_idx:     device, int32 [num_tokens, topk] (the dispatch routing;
+ *                 an entry outside [0, num_experts) is masked).
+ *   topk_weights: device, fp32 [num_tokens, topk].
+ *   out:          device, fp32 [num_tokens, hidden], 16-byte aligned; may
+ *                 not overlap the layout.
+ *   max_spins:    >= 1; polls of one flag before its wait gives up.
+ *   refusal:      device, int32, 4-byte aligned, zeroed by the caller
+ *                 (may be NULL when num_tokens is 0).
+ * out[t, c] = fma chain over the routed k in ascending order, from +0.0f,
+ * of acc = fmaf(w[t, k], bf16 column c of staging row e * max_tokens + t,
+ * acc), in fp32: the same expression, and so the same bits, as
+ * ll_moe_combine on the same routing and expert outputs.
+ * A wait that runs out ORs LL_MOE_REFUSAL_FLAG_WAIT into *refusal, and
+ * out is then unspecified (rows of that token, and of later tokens that the
+ * same workgroup serves, may be left unwritten); every wait is bounded, so
+ * the launch always ends. Order: after the dispatch of set q (its counts must
+ * be final); it may run at the same time as ll_moe_combine_send of set q on
+ * another stream and then waits for its flags (if it holds the GPU resources
+ * the expert side needs to start, the waits run out into a refusal).
+ * Enqueued on `stream`.
+ */
+int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden,
+                        int num_experts, int topk, int dtype, int parity,
+                        const int32_t* topk_idx, const float* topk_weights, float* out,
+                        int max_spins, int32_t* refusal, hipStream_t stream);
+
+/*
  * ll_moe_clean_signals — zero the num_experts int64 signal words of set
  * `parity` (the rocSHMEM example's clean_meta(): the dispatch count words
  * and the combine flag words are one array). Enqueued on `stream`.

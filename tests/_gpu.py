@@ -86,6 +86,58 @@ class Step:
         torch.cuda.synchronize()
         return out.cpu().numpy(), ref
 
+    def combine_send(self, q, y: np.ndarray, y_dev=None, stream=None):
+        w = self.w
+        yd = to_dev(y) if y_dev is None else y_dev
+        ll.ll_moe_combine_send(self.lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, yd,
+                               stream=stream)
+        oracle.combine_send(self.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, y)
+
+    def combine_recv(self, q, idx: np.ndarray, wt: np.ndarray, max_spins=1 << 22, stream=None,
+                     with_oracle=True):
+        """Token side on the GPU (and the oracle's, unless with_oracle is
+        False); returns (out, refusal word, oracle out or None) once the
+        GPU is done."""
+        w = self.w
+        n = idx.shape[0]
+        out = torch.full((n, w.hidden), float("nan"), dtype=torch.float32, device=DEV)
+        refusal = torch.zeros(1, dtype=torch.int32, device=DEV)
+        ll.ll_moe_combine_recv(self.lay, w.capacity, n, w.hidden, w.num_experts, idx.shape[1],
+                               w.dtype, q, to_dev(idx), to_dev(wt), out, max_spins, refusal,
+                               stream=stream)
+        ref = None
+        if with_oracle:
+            ref = oracle.combine_recv(self.img, w.capacity, w.hidden, w.num_experts, w.dtype, q,
+                                      idx, wt)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), int(refusal.item()), ref
+
+    def check_staging(self, q, idx: np.ndarray):
+        """Set q's staging rows of every routed (t, k) against the oracle,
+        and the whole layout when the image is kept in full."""
+        torch.cuda.synchronize()
+        self.check_signals()
+        w, mc = self.w, self.mc
+        if self.full:
+            gi = host_u8(self.lay)
+            if not np.array_equal(gi, self.img):
+                bad = np.nonzero(gi != self.img)[0]
+                raise AssertionError(f"layout image differs at {bad.size} bytes, first {bad[0]}")
+            return
+        e = idx.astype(np.int64)
+        t = np.broadcast_to(np.arange(idx.shape[0])[:, None], idx.shape)
+        ok = (e >= 0) & (e < w.num_experts)
+        rows = np.unique(e[ok] * w.capacity + t[ok])
+        nrow = w.num_experts * w.capacity
+        stage = self.L["send"][q]
+        sv = self.lay[stage:stage + nrow * mc].view(nrow, mc)
+        g = host_u8(sv.index_select(0, torch.from_numpy(rows).to(DEV)))
+        r = self.img[stage:stage + nrow * mc].reshape(nrow, mc)[rows]
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError(f"staging rows differ: {bad.shape[0]} bytes, first (row "
+                                 f"{rows[bad[0][0]]}, col {bad[0][1]})")
+
     # -- comparisons ---------------------------------------------------------
     def signals(self, q):
         off = self.L["sig"][q]

@@ -121,6 +121,43 @@ def test_watch_rejects_bad_arguments(case):
     assert rc == ll.INVALID_ARGUMENT
 
 
+BIG = 1 << 36  # far above any FAKE layout: never overlaps it
+
+
+@pytest.mark.parametrize("case", [
+    dict(parity=2), dict(hidden=1020), dict(dtype=7), dict(dtype=1, hidden=1000),
+    dict(layout=0), dict(layout=FAKE + 8), dict(y=0), dict(y=BIG + 8),
+    dict(num_experts=4097), dict(max_tokens=0), dict(hidden=22528),
+    dict(y=FAKE + 64),  # overlaps the layout
+    dict(max_tokens=1 << 20, num_experts=4096),  # num_experts * max_tokens >= 2^31
+])
+def test_combine_send_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, hidden=1024, num_experts=8, dtype=0, parity=0, y=BIG)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_combine_send", a["layout"], a["max_tokens"], a["hidden"],
+                       a["num_experts"], a["dtype"], a["parity"], a["y"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("case", [
+    dict(parity=2), dict(num_tokens=129), dict(num_tokens=-1), dict(topk=0), dict(topk=9),
+    dict(hidden=1020), dict(hidden=22528), dict(num_experts=4097, topk=2), dict(layout=0),
+    dict(layout=FAKE + 4), dict(idx=0), dict(idx=BIG + 2), dict(w=0), dict(w=BIG + 1),
+    dict(out=0), dict(out=2 * BIG + 4), dict(out=FAKE + 64), dict(max_spins=0),
+    dict(max_spins=-5), dict(refusal=0), dict(refusal=3 * BIG + 2),
+])
+def test_combine_recv_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
+             dtype=0, parity=0, idx=BIG, w=BIG, out=2 * BIG, max_spins=100, refusal=3 * BIG)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_combine_recv", a["layout"], a["max_tokens"], a["num_tokens"],
+                       a["hidden"], a["num_experts"], a["topk"], a["dtype"], a["parity"],
+                       a["idx"], a["w"], a["out"], a["max_spins"], a["refusal"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 def test_binding_routes_through_the_library_only():
     """The binding imports neither the oracle nor the workload generators."""
     src = open(os.path.join(ROOT, "combine_ll_moe_amd", "__init__.py")).read()
