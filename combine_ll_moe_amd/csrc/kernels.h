@@ -93,6 +93,7 @@ constexpr int kXcds = 8;  // XCDs of an MI355X; workgroups are dealt to them rou
 // Buffer-store cache policy with the device-scope coherence bit (sc1): the
 // store writes through the XCD's L2. Raw-buffer descriptor word 3 for gfx9.
 constexpr int kCachePolicySc1 = 16;
+constexpr int kCachePolicyNt = 2;  // non-temporal (streaming)
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
 constexpr int kCombineBlock = 256;
