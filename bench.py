@@ -41,14 +41,30 @@ def algorithmic_bytes(w, md: int, routed: int) -> dict:
             "dispatch_writes": n * md + routed * md}
 
 
-KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel"}
+def two_phase_bytes(w, md: int, routed: int) -> dict:
+    """Bytes the two-phase combine must move per step.
+    send (expert side): read the counts, each routed receive row's header
+      and its expert-output row (bf16); write the staging rows (combine
+      messages) and raise the flags; clean the other set's words.
+    recv (token side): read the routing, weights and flags, the staged
+      payloads (bf16), and write the fp32 output; clean the other set."""
+    n, h, e, k = w.num_tokens, w.hidden, w.num_experts, w.topk
+    mc = 4 + 2 * h
+    send = 8 * e + routed * 4 + routed * h * 2 + routed * mc + 8 * e + 8 * e
+    recv = 8 * n * k + 8 * routed + routed * h * 2 + 4 * n * h + 8 * e
+    return {"send": send, "recv": recv}
+
+
+KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
+                "send": "combine_send_kernel", "recv": "combine_recv_kernel"}
 COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                              "hbm_counters.json")
 
 
 # The sources of the dispatch / combine path (launch shapes included); the
 # diagnostic kernels are not part of it.
-PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "kernels.h", "layout.h", "route.h")
+PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "kernels.h", "layout.h", "message.h",
+                "route.h", "two_phase.hip")
 
 
 def kernel_source_hash() -> str:
@@ -134,9 +150,10 @@ def summarize_profiles(args) -> None:
     w = W.WORKLOADS[args.workload]
     md = (4 + 2 * w.hidden) if w.dtype == W.BF16 else (4 + w.hidden + w.hidden // 32)
     ab = algorithmic_bytes(w, md, w.num_tokens * w.topk)
+    ab.update(two_phase_bytes(w, md, w.num_tokens * w.topk))
     f_fetch = copy["fetch_kib"] * 1024.0 / copy["bytes"]
     f_write = copy["write_kib"] * 1024.0 / copy["bytes"]
-    lines = [f"# {args.workload}: dispatch and combine kernels (rocprofv3)", "",
+    lines = [f"# {args.workload}: dispatch, combine and two-phase combine kernels (rocprofv3)", "",
              f"Workload: {w.name}, N={w.num_tokens}, hidden={w.hidden}, experts={w.num_experts}, "
              f"top-k={w.topk}, payload {'bf16' if w.dtype == W.BF16 else 'fp8 e4m3'}.", "",
              "## Kernel durations (`--kernel-trace --stats`)", "",
@@ -157,13 +174,20 @@ def summarize_profiles(args) -> None:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             cur.setdefault(r["Kernel_Name"], []).append(d)
     titles = ["dispatch + combine steps", "dispatch back to back (roofline timing)",
-              "combine back to back (roofline timing)",
+              "combine back to back (roofline timing), then the two-phase warm-up steps",
+              "two-phase steps (dispatch, combine_send, combine_recv), then one step preparing set 0",
+              "combine_send back to back on one set, then one step preparing set 0",
+              "combine_recv back to back on one set",
               "cold: after a 512 MiB eviction, event pairs between launches",
               "warm, the same event pairs between launches"]
     lines += ["", "## The same launches by timed region of bench.py", "",
+              "Each region starts after a stream hold (a spin kernel), queued behind two "
+              "signal-word cleans (not listed).", "",
               "| region | kernel | calls | average us |", "|---|---|---|---|"]
     for title, seg in zip(titles, segs):
         for name, ds in seg.items():
+            if "clean_kernel" in name:  # the set resets queued before each hold
+                continue
             lines.append(f"| {title} | `{name[:60]}` | {len(ds)} | {sum(ds) / len(ds):.2f} |")
     lines += ["", "## HBM bytes per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
               f"Calibration: a plain {copy['bytes']} B device copy (`{copy_name[:60]}`) read "
@@ -264,6 +288,8 @@ def main():
                     help="further timed repetitions of the K steps (median and min reported)")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the plain-kernel context timings (empty launch, fill, copy)")
+    ap.add_argument("--no-two-phase", action="store_true",
+                    help="skip the two-phase combine timings")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed after evicting L2 and MALL (0: skip)")
     ap.add_argument("--summarize-profiles", action="store_true",
@@ -354,7 +380,16 @@ def main():
     # sizes, so a short spin kernel first holds the stream while the timed
     # launches are queued behind it: the events then time the GPU running
     # the steps back to back, not the host's launch rate.
-    def hold_stream():
+    # Every timed region starts from clean signal words (a dispatch of set q
+    # needs set q's words at zero) and runs its steps with parity 0, 1, ...
+    def reset_sets():
+        for q in (0, 1):
+            ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, sptr)
+
+    def hold_stream(prepare=None):
+        reset_sets()
+        if prepare is not None:
+            prepare()
         torch.cuda._sleep(HOLD_CYCLES)
 
     # timed region: K back-to-back steps, nothing else between them
@@ -374,10 +409,10 @@ def main():
 
     # per-kernel launch times: K launches of one kernel back to back (parity
     # alternating, as in the step), timed on the stream they run on
-    def time_kernel(fn):
+    def time_kernel(fn, prepare=None):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        hold_stream()
+        hold_stream(prepare)
         a.record(stream)
         for s in range(args.steps):
             fn(s)
@@ -390,16 +425,19 @@ def main():
     print(f"[bench] dispatch {d_us:.2f} us/launch, combine {c_us:.2f} us/launch",
           file=sys.stderr, flush=True)
 
-    # the same K steps captured once as a HIP graph and replayed
+    # the same steps captured once as a HIP graph and replayed back to back
+    # (an even number of them, so that every replay starts on a clean set 0)
     graph_us = None
     if not args.no_graph:
+        gsteps = args.steps + (args.steps & 1)
+        reset_sets()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
                 gs = torch.cuda.current_stream().cuda_stream
-                for s in range(args.steps):
+                for s in range(gsteps):
                     x, idx, wt = batches[s % len(batches)]
                     ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
                                        w.topk, w.dtype, s & 1, x, idx, gs)
@@ -415,7 +453,7 @@ def main():
             g.replay()
             b.record(stream)
             torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / args.steps
+            us = a.elapsed_time(b) * 1e3 / gsteps
             best = us if best is None else min(best, us)
         graph_us = best
         print(f"[bench] graph replay: {graph_us:.2f} us/step", file=sys.stderr, flush=True)
@@ -433,6 +471,54 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         trials.append(a.elapsed_time(b) * 1e3 / args.steps)
+
+    # the two-phase combine on the same batches: a step is dispatch(q),
+    # combine_send(q), combine_recv(q); then each side alone, K launches
+    # back to back on one set (the expert side re-stages the same rows, its
+    # flags counting past the counts; the token side re-folds raised flags)
+    two_phase = None
+    if not args.no_two_phase:
+        refusal = torch.zeros(1, dtype=torch.int32, device=dev)
+        spins = 1 << 20
+
+        def send(s):
+            ll.ll_moe_combine_send(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1, y,
+                                   sptr)
+
+        def recv(s):
+            _, idx, wt = batches[s % len(batches)]
+            ll.ll_moe_combine_recv(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                   w.topk, w.dtype, s & 1, idx, wt, out, spins, refusal, sptr)
+
+        def tp_step(s):
+            dispatch(s)
+            send(s)
+            recv(s)
+
+        reset_sets()
+        for s in range(args.warmup):
+            tp_step(s)
+        tp_us = time_kernel(tp_step)
+        tp_ok = int(refusal.item()) == 0
+        # set 0 prepared after the region's reset: one step's counts and flags
+        send_us = time_kernel(lambda s: send(0), prepare=lambda: tp_step(0))
+        recv_us = time_kernel(lambda s: recv(0), prepare=lambda: tp_step(0))
+        tp_ok = tp_ok and int(refusal.item()) == 0
+        for q in (0, 1):
+            ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q)
+        torch.cuda.synchronize()
+        tb = two_phase_bytes(w, md, routed[0])
+        two_phase = {
+            "us_per_step": round(tp_us, 3),
+            "fused_us_per_step": round(ms_per_step * 1e3, 3),
+            "send_us": round(send_us, 3), "recv_us": round(recv_us, 3),
+            "send_gbs": round(tb["send"] / (send_us * 1e-6) / 1e9, 2),
+            "recv_gbs": round(tb["recv"] / (recv_us * 1e-6) / 1e9, 2),
+            "bytes_per_launch": tb, "refusals": not tp_ok,
+            "traffic": {"send": stored_traffic(w.name, "send"),
+                        "recv": stored_traffic(w.name, "recv")}}
+        print(f"[bench] two-phase: {tp_us:.2f} us/step (send {send_us:.2f}, recv {recv_us:.2f}); "
+              f"fused {ms_per_step * 1e3:.2f}", file=sys.stderr, flush=True)
 
     # cold steps: the decode working set fits in the 256 MB MALL, so back to
     # back the step runs from cache; here a 512 MiB write evicts L2 and MALL
@@ -512,6 +598,7 @@ def main():
                            "median": round(float(np.median(trials)), 3) if trials else None,
                            "min": round(min(trials), 3) if trials else None},
         "cold": cold,
+        "two_phase_combine": two_phase,
         "floors": floors,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
