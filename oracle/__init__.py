@@ -43,6 +43,7 @@ def lib():
         L.oracle_clean.argtypes = [vp, i, i, i, i, i]
         L.oracle_combine_send.argtypes = [vp, i, i, i, i, i, vp]
         L.oracle_combine_recv.argtypes = [vp, i, i, i, i, i, i, i, vp, vp, vp]
+        L.oracle_dispatch_recv.argtypes = [vp, i, i, i, i, i, i, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -169,6 +170,38 @@ def combine_recv(image, max_tokens, hidden, num_experts, dtype, parity, idx, wei
     if rc != 0:
         raise ValueError("oracle combine_recv rejected its arguments")
     return out
+
+
+class CountsIncomplete(RuntimeError):
+    """The dispatch's expert side needs counts that add up to the expected
+    number of messages (the GPU reports this in its refusal word)."""
+
+
+def dispatch_recv(image, max_tokens, hidden, num_experts, dtype, parity, expected, out=None):
+    """Expert side of the dispatch: unpack set `parity`'s received messages.
+    Returns (payload u8 [E*Nmax, row bytes], scales f32 [E*Nmax, h/128] or
+    None, src int32 [E*Nmax], counts int32 [E]); `out` may hold those four
+    arrays pre-filled (rows the step does not write keep their contents)."""
+    rows = num_experts * max_tokens
+    pb = 2 * hidden if dtype == 0 else hidden
+    if out is None:
+        out = (np.zeros((rows, pb), np.uint8),
+               np.zeros((rows, hidden // 128), np.float32) if dtype == 1 else None,
+               np.zeros(rows, np.int32), np.zeros(num_experts, np.int32))
+    payload, scales, src, counts = out
+    assert payload.shape == (rows, pb) and payload.dtype == np.uint8
+    assert src.shape == (rows,) and counts.shape == (num_experts,)
+    if dtype == 1:
+        assert scales.shape == (rows, hidden // 128) and scales.dtype == np.float32
+    rc = lib().oracle_dispatch_recv(_ptr(image), max_tokens, hidden, num_experts, dtype, parity,
+                                    expected, _ptr(payload),
+                                    _ptr(scales) if scales is not None else None, _ptr(src),
+                                    _ptr(counts))
+    if rc == -2:
+        raise CountsIncomplete("the counts do not add up to the expected messages")
+    if rc != 0:
+        raise ValueError("oracle dispatch_recv rejected its arguments")
+    return payload, scales, src, counts
 
 
 def clean(image, max_tokens, hidden, num_experts, dtype, parity):

@@ -488,6 +488,58 @@ int oracle_combine_recv(uint8_t* image, int max_tokens, int num_tokens, int hidd
 }
 
 /* ---------------------------------------------------------------------------
+ * Expert side of the dispatch with parity q: wait for the dispatch's
+ * messages, then unpack them into the form an expert's matrix product
+ * reads. The pages give the receive rows, the per-expert counts and
+ * [mscclpp.h]'s rule that a receiver reads only after the signal, not this
+ * step; the readings taken:
+ *  - the receiver knows how many messages the step routes (`expected`) and
+ *    takes set q as complete when the counts (low halves of its signal
+ *    words) add up to that number. A partial count does not tell which of
+ *    an expert's slots are written; the sum reaching the total does;
+ *  - unpacked, receive row r = e * max_tokens + j (j below count_e) gives
+ *    its payload without the header in a row of its own (bf16: the 2h bytes
+ *    of x; fp8: the h codes, and the h/128 fp32 scales in a second array),
+ *    its header in an int32 array, and count_e goes to an int32 array.
+ *    Bytes move unchanged; rows at or past count_e are not written;
+ *  - a count above max_tokens is taken as max_tokens.
+ * The launch zeroes the other set's signal words first, as every launch of
+ * parity q does. Returns -2 (and writes no output) when the counts do not
+ * add up to `expected`: the GPU side reports that in a refusal word after
+ * a bounded wait.
+ * ------------------------------------------------------------------------- */
+int oracle_dispatch_recv(uint8_t* image, int max_tokens, int hidden, int num_experts,
+                         int dtype, int parity, int expected, uint8_t* payload,
+                         float* scales, int32_t* src, int32_t* counts) {
+  uint64_t lay[7], md, mc;
+  if (check_call(max_tokens, 0, hidden, num_experts, 1, dtype, parity, lay) != 0)
+    return -1;
+  oracle_message_bytes(hidden, dtype, &md, &mc);
+  const uint8_t* recv = image + lay[3 + parity];
+  const uint8_t* sig = image + lay[5 + parity];
+  uint8_t* sig_other = image + lay[5 + (parity ^ 1)];
+  for (int e = 0; e < num_experts; ++e) put_i64(sig_other + 8 * (uint64_t)e, 0);
+  int64_t total = 0;
+  for (int e = 0; e < num_experts; ++e) total += get_i64(sig + 8 * (uint64_t)e) & 0xFFFFFFFF;
+  if (total != (int64_t)expected) return -2;
+  const uint64_t row_bytes = dtype == OR_BF16 ? 2 * (uint64_t)hidden : (uint64_t)hidden;
+  const uint64_t nscales = (uint64_t)hidden / OR_FP8_BLOCK;
+  for (int e = 0; e < num_experts; ++e) {
+    int64_t c = get_i64(sig + 8 * (uint64_t)e) & 0xFFFFFFFF;
+    if (c > max_tokens) c = max_tokens;
+    counts[e] = (int32_t)c;
+    for (int64_t j = 0; j < c; ++j) {
+      const uint64_t r = (uint64_t)e * (uint64_t)max_tokens + (uint64_t)j;
+      const uint8_t* row = recv + r * md;
+      memcpy(&src[r], row, 4);
+      memcpy(payload + r * row_bytes, row + 4, row_bytes);
+      if (dtype == OR_FP8_E4M3) memcpy(scales + r * nscales, row + 4 + hidden, 4 * nscales);
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Explicit clean of set q's signal words: [rocSHMEM LL_MoE_Buffers.hpp,
  * clean_meta()] returns the signal pointer and num_sig_elems (= experts)
  * words to zero.
