@@ -502,7 +502,8 @@ int oracle_combine_recv(uint8_t* image, int max_tokens, int num_tokens, int hidd
  *    of x; fp8: the h codes, and the h/128 fp32 scales in a second array),
  *    its header in an int32 array, and count_e goes to an int32 array.
  *    Bytes move unchanged; rows at or past count_e are not written;
- *  - a count above max_tokens is taken as max_tokens.
+ *  - a count above max_tokens is taken as max_tokens, in the sum as in the
+ *    unpacking.
  * The launch zeroes the other set's signal words first, as every launch of
  * parity q does. Returns -2 (and writes no output) when the counts do not
  * add up to `expected`: the GPU side reports that in a refusal word after
@@ -520,7 +521,10 @@ int oracle_dispatch_recv(uint8_t* image, int max_tokens, int hidden, int num_exp
   uint8_t* sig_other = image + lay[5 + (parity ^ 1)];
   for (int e = 0; e < num_experts; ++e) put_i64(sig_other + 8 * (uint64_t)e, 0);
   int64_t total = 0;
-  for (int e = 0; e < num_experts; ++e) total += get_i64(sig + 8 * (uint64_t)e) & 0xFFFFFFFF;
+  for (int e = 0; e < num_experts; ++e) {
+    int64_t c = get_i64(sig + 8 * (uint64_t)e) & 0xFFFFFFFF;
+    total += c > max_tokens ? max_tokens : c;
+  }
   if (total != (int64_t)expected) return -2;
   const uint64_t row_bytes = dtype == OR_BF16 ? 2 * (uint64_t)hidden : (uint64_t)hidden;
   const uint64_t nscales = (uint64_t)hidden / OR_FP8_BLOCK;

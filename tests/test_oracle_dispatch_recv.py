@@ -126,3 +126,27 @@ def test_clean_set_unpacks_nothing():
     payload, _, src, counts = oracle.dispatch_recv(img, w.capacity, w.hidden, w.num_experts,
                                                    w.dtype, 0, 0, out=out)
     assert (counts == 0).all() and (src == -7).all() and (payload == SENT).all()
+
+
+def test_count_above_capacity_is_taken_as_capacity():
+    """A count word above max_tokens (not something a dispatch writes) is
+    read as max_tokens, in the completion sum and in the unpacking."""
+    w = W.WORKLOADS["tiny"]
+    img = oracle.new_image(w.capacity, w.hidden, w.num_experts, w.dtype, fill=SENT)
+    for p in (0, 1):
+        oracle.clean(img, w.capacity, w.hidden, w.num_experts, w.dtype, p)
+    L = oracle.layout(w.capacity, w.hidden, w.num_experts, w.dtype)
+    sig = img[L["sig"][0]:L["sig"][0] + 8 * w.num_experts].view(np.int64)
+    sig[3] = w.capacity + 50
+    sig[5] = 7 | (123 << 32)  # a flag in the high half does not count
+    with pytest.raises(oracle.CountsIncomplete):
+        oracle.dispatch_recv(img, w.capacity, w.hidden, w.num_experts, w.dtype, 0,
+                             w.capacity + 57)
+    _, _, src, counts = oracle.dispatch_recv(img, w.capacity, w.hidden, w.num_experts, w.dtype,
+                                             0, w.capacity + 7)
+    assert counts.tolist() == [0, 0, 0, w.capacity, 0, 7, 0, 0]
+    rows = 3 * w.capacity + np.arange(w.capacity)
+    recv = L["recv"][0]
+    md, _ = oracle.message_bytes(w.hidden, w.dtype)
+    hdr = [int(img[recv + r * md:recv + r * md + 4].view(np.int32)[0]) for r in rows]
+    assert src[rows].tolist() == hdr
