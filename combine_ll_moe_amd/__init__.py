@@ -27,6 +27,7 @@ MAX_MESSAGE_BYTES = 45056
 MAX_EXPERTS = 1 << 20
 SEND_MAX_EXPERTS = 4096
 REFUSAL_FLAG_WAIT = 1
+REFUSAL_COUNT_WAIT = 2
 
 SUCCESS = 0
 HIP_ERROR = 1
@@ -45,13 +46,15 @@ _lib.ll_moe_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, 
 _lib.ll_moe_combine_send.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
 _lib.ll_moe_combine_recv.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp,
                                      _vp]
+_lib.ll_moe_dispatch_recv.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp,
+                                      _vp]
 _lib.ll_moe_clean_signals.argtypes = [_vp, _i, _i, _i, _i, _i, _vp]
 _lib.ll_moe_diag_e4m3.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 _lib.ll_moe_diag_watch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]
 _lib.ll_moe_status_string.argtypes = [_i]
 _lib.ll_moe_status_string.restype = ctypes.c_char_p
 for _f in ("ll_moe_layout_bytes", "ll_moe_layout_offsets", "ll_moe_dispatch",
-           "ll_moe_combine", "ll_moe_combine_send", "ll_moe_combine_recv",
+           "ll_moe_combine", "ll_moe_combine_send", "ll_moe_combine_recv", "ll_moe_dispatch_recv",
            "ll_moe_clean_signals", "ll_moe_diag_e4m3", "ll_moe_diag_watch"):
     getattr(_lib, _f).restype = _i
 
@@ -130,6 +133,15 @@ def ll_moe_combine_recv(layout, max_tokens: int, num_tokens: int, hidden: int, n
                                     topk, dtype, parity, _ptr(topk_idx), _ptr(topk_weights),
                                     _ptr(out), max_spins, _ptr(refusal), _stream(stream)),
            "ll_moe_combine_recv")
+
+
+def ll_moe_dispatch_recv(layout, max_tokens: int, hidden: int, num_experts: int, dtype: int,
+                         parity: int, expected: int, payload, scales, src_tokens, counts,
+                         max_spins: int, refusal, stream=None) -> None:
+    _check(_lib.ll_moe_dispatch_recv(_ptr(layout), max_tokens, hidden, num_experts, dtype, parity,
+                                     expected, _ptr(payload), _ptr(scales), _ptr(src_tokens),
+                                     _ptr(counts), max_spins, _ptr(refusal), _stream(stream)),
+           "ll_moe_dispatch_recv")
 
 
 def ll_moe_clean_signals(layout, max_tokens: int, hidden: int, num_experts: int, dtype: int,

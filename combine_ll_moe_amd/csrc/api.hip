@@ -6,6 +6,7 @@
 
 #include "ll_moe.h"
 #include "ll_moe_diag.h"
+#include "expert.h"
 #include "kernels.h"
 #include "layout.h"
 #include "route.h"
@@ -205,8 +206,7 @@ extern "C" int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int
   p.msg_bytes = (uint32_t)L.dispatch_msg;
   p.comb_bytes = (uint32_t)L.combine_msg;
   // LDS: the count prefix, then one or two message buffers
-  const int rounds = num_experts <= kSendBlock ? 1 : num_experts <= 4 * kSendBlock ? 4 : 16;
-  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
+  const uint32_t prefix_bytes = count_prefix_bytes(num_experts);
   const uint32_t stride = ((uint32_t)kMsgLdsOffset + p.comb_bytes + 15u) & ~15u;
   p.nbuf = prefix_bytes + 2 * stride <= 65536u - 64u ? 2 : 1;
   const int64_t most_rows = (int64_t)num_experts * max_tokens;
@@ -254,6 +254,60 @@ extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens,
   p.max_spins = max_spins;
   p.stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
   return from_hip(launch_combine_recv(p, stream));
+}
+
+namespace {
+// Expert side of the dispatch: a fixed grid, one workgroup per CU, so that
+// while it waits beside a running dispatch it leaves the dispatch room.
+constexpr int kUnpackBlocks = 256;
+}  // namespace
+
+extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
+                                    int dtype, int parity, int expected, void* payload,
+                                    float* scales, int32_t* src_tokens, int32_t* counts,
+                                    int max_spins, int32_t* refusal, hipStream_t stream) {
+  Layout L;
+  int rc = check_shape(max_tokens, 0, hidden, num_experts, 1, dtype, parity, &L);
+  if (rc != LL_MOE_SUCCESS) return rc;
+  if (dtype == kBf16 && hidden % 8 != 0) return LL_MOE_INVALID_ARGUMENT;
+  if (num_experts > LL_MOE_SEND_MAX_EXPERTS) return LL_MOE_INVALID_ARGUMENT;
+  const int64_t slots = (int64_t)num_experts * max_tokens;
+  if (slots > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
+  if (expected < 0 || expected > slots || max_spins < 1) return LL_MOE_INVALID_ARGUMENT;
+  if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
+  if (!payload || !src_tokens || !counts || !refusal) return LL_MOE_INVALID_ARGUMENT;
+  if (dtype == kFp8 && !scales) return LL_MOE_INVALID_ARGUMENT;
+  if (!aligned(payload, 16) || !aligned(src_tokens, 4) || !aligned(counts, 4) ||
+      !aligned(refusal, 4) || (dtype == kFp8 && !aligned(scales, 4)))
+    return LL_MOE_INVALID_ARGUMENT;
+  const uint64_t row_bytes = dtype == kBf16 ? 2 * (uint64_t)hidden : (uint64_t)hidden;
+  // the outputs are written while the layout is read: no overlap
+  if (overlaps(layout, L.total, payload, slots * row_bytes) ||
+      overlaps(layout, L.total, src_tokens, slots * 4) ||
+      overlaps(layout, L.total, counts, (uint64_t)num_experts * 4) ||
+      (dtype == kFp8 && overlaps(layout, L.total, scales, slots * (hidden / 128) * 4)))
+    return LL_MOE_INVALID_ARGUMENT;
+
+  uint8_t* base = static_cast<uint8_t*>(layout);
+  UnpackParams p;
+  p.sig = reinterpret_cast<const unsigned long long*>(base + L.sig_off(parity));
+  p.sig_other = reinterpret_cast<unsigned long long*>(base + L.sig_off(parity ^ 1));
+  p.recv = base + L.recv_off(parity);
+  p.payload = static_cast<uint8_t*>(payload);
+  p.scales = scales;
+  p.src = src_tokens;
+  p.counts = counts;
+  p.refusal = refusal;
+  p.max_tokens = max_tokens;
+  p.hidden = hidden;
+  p.num_experts = num_experts;
+  p.fp8 = dtype == kFp8;
+  p.msg_bytes = (uint32_t)L.dispatch_msg;
+  p.row_bytes = (uint32_t)row_bytes;
+  p.expected = expected;
+  p.max_spins = max_spins;
+  const int blocks = slots < kUnpackBlocks ? (int)slots : kUnpackBlocks;
+  return from_hip(launch_dispatch_recv(p, blocks, stream));
 }
 
 extern "C" int ll_moe_clean_signals(void* layout, int max_tokens, int hidden, int num_experts,

@@ -77,11 +77,32 @@ struct RecvParams {                // two-phase combine, token side
   int stream_rows;                 // read the staging rows with non-temporal loads
 };
 
+struct UnpackParams {              // expert side of the dispatch
+  const unsigned long long* sig;   // signal words of set q (counts in the low halves)
+  unsigned long long* sig_other;   // signal words of set 1-q (zeroed)
+  const uint8_t* recv;             // receive buffer of set q
+  uint8_t* payload;                // [num_experts * max_tokens, row_bytes]
+  float* scales;                   // fp8: [num_experts * max_tokens, hidden / 128]
+  int32_t* src;                    // [num_experts * max_tokens] source tokens
+  int32_t* counts;                 // [num_experts]
+  int32_t* refusal;                // refusal word: set when the wait runs out
+  int max_tokens;
+  int hidden;
+  int num_experts;
+  int fp8;                         // payload = hidden e4m3 codes, then hidden/128 scales
+  uint32_t msg_bytes;              // md
+  uint32_t row_bytes;              // payload bytes of one unpacked row
+  int expected;                    // messages the step routes
+  int max_spins;                   // polls of the counts before the wait gives up
+};
+
 // The two-phase combine's expert side keeps every expert's count in LDS.
 constexpr int kSendMaxExperts = 4096;
 constexpr int kSendBlock = 256;
-// Refusal code of ll_moe_combine_recv: a flag wait ran out.
+// Refusal codes: a flag wait of ll_moe_combine_recv ran out; the count wait
+// of ll_moe_dispatch_recv ran out.
 constexpr int32_t kRefusalFlagWait = 1;
+constexpr int32_t kRefusalCountWait = 2;
 
 // LDS placement of a message: it starts at this offset of its buffer, so
 // that the payload (message byte 4) is 16-byte aligned; a buffer is
@@ -102,6 +123,7 @@ hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t strea
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream);
 hipError_t launch_combine_recv(const RecvParams& p, hipStream_t stream);
+hipError_t launch_dispatch_recv(const UnpackParams& p, int blocks, hipStream_t stream);
 hipError_t launch_clean(unsigned long long* sig, int num_experts, hipStream_t stream);
 hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, hipStream_t stream);
 

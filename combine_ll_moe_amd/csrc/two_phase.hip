@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "expert.h"
 #include "kernels.h"
 #include "message.h"
 #include "route.h"
@@ -49,71 +50,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Rows at or above this many bytes go out with whole-cache-line lane
 // mapping (mostly HBM-bound writes); smaller ones stay in the caches.
 constexpr uint64_t kSendLineBytes = 64ull << 20;
-
-// Exclusive prefix of the counts (low halves of the signal words, each
-// taken as at most max_tokens) into pre[0..E], pre[E] = total rows.
-// ROUNDS * kSendBlock >= E. Thread tid loads experts tid + r * kSendBlock
-// (coalesced, all loads issued before any is used), the counts go to LDS,
-// then thread tid sums the contiguous run [tid * ROUNDS, (tid + 1) * ROUNDS)
-// and a workgroup scan of the run sums gives each run its base.
-template <int ROUNDS>
-__device__ __forceinline__ void count_prefix(const SendParams& P, uint32_t* pre,
-                                             uint32_t* wave_sum) {
-  const int tid = threadIdx.x;
-  const int E = P.num_experts;
-  uint32_t c[ROUNDS];
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int e = tid + r * kSendBlock;
-    const uint64_t w = __hip_atomic_load(P.sig + (e < E ? e : E - 1), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t n = (uint32_t)w;
-    c[r] = e < E ? (n < (uint32_t)P.max_tokens ? n : (uint32_t)P.max_tokens) : 0u;
-  }
-  // No acquire fence: the counts, headers and expert rows come from kernels
-  // ordered before this one (stream order or events), and a kernel boundary
-  // already makes their writes visible. An in-kernel acquire at device scope
-  // invalidates the XCD's L2; one per workgroup costs ~27 us per launch.
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) pre[tid + r * kSendBlock] = c[r];
-  __syncthreads();
-  uint32_t run[ROUNDS];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < ROUNDS; ++i) {
-    run[i] = sum;
-    sum += pre[tid * ROUNDS + i];
-  }
-  // inclusive scan of the run sums within the wavefront, then across waves
-  const int lane = tid & (kWave - 1);
-  uint32_t incl = sum;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  if (lane == kWave - 1) wave_sum[tid / kWave] = incl;
-  __syncthreads();
-  uint32_t base = incl - sum;
-  for (int w = 0; w < tid / kWave; ++w) base += wave_sum[w];
-#pragma unroll
-  for (int i = 0; i < ROUNDS; ++i) pre[tid * ROUNDS + i] = base + run[i];
-  if (tid == kSendBlock - 1) pre[kSendBlock * ROUNDS] = base + sum;
-  __syncthreads();
-}
-
-// Expert of flattened row r: the largest e < E with pre[e] <= r (an expert
-// with no rows has pre[e] == pre[e + 1], so it is never the answer for a
-// row below pre[E]).
-__device__ __forceinline__ int expert_of_row(const uint32_t* pre, int E, uint32_t r) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= r) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
 
 template <bool LINE>
 __device__ __forceinline__ void stage_rows(const SendParams& P, uint32_t* pre, uint8_t* lds_msg,
@@ -190,22 +126,17 @@ __global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendPara
   if (blockIdx.x == 0)
     for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
 
+  // No acquire fence: the counts, headers and expert rows come from kernels
+  // ordered before this one (stream order or events), and a kernel boundary
+  // already makes their writes visible. An in-kernel acquire at device scope
+  // invalidates the XCD's L2; one per workgroup costs ~27 us per launch.
   uint32_t* pre = reinterpret_cast<uint32_t*>(lds_raw);
-  if (P.num_experts <= kSendBlock)
-    count_prefix<1>(P, pre, wave_sum);
-  else if (P.num_experts <= 4 * kSendBlock)
-    count_prefix<4>(P, pre, wave_sum);
-  else
-    count_prefix<kSendMaxExperts / kSendBlock>(P, pre, wave_sum);
-  // pre[kSendBlock * ROUNDS] is the total; rows beyond E have zero counts
-  const int rounds = P.num_experts <= kSendBlock ? 1 : P.num_experts <= 4 * kSendBlock ? 4 : 16;
-  const uint32_t rows = pre[kSendBlock * rounds];
+  const uint32_t rows = load_count_prefix(P.sig, P.num_experts, P.max_tokens, pre, wave_sum);
 
   const uint32_t r0 = (uint32_t)((uint64_t)rows * blockIdx.x / gridDim.x);
   const uint32_t r1 = (uint32_t)((uint64_t)rows * (blockIdx.x + 1) / gridDim.x);
   if (r0 >= r1) return;
-  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
-  uint8_t* lds_msg = lds_raw + prefix_bytes + kMsgLdsOffset;
+  uint8_t* lds_msg = lds_raw + count_prefix_bytes(P.num_experts) + kMsgLdsOffset;
   const uint32_t msg_stride = ((uint32_t)kMsgLdsOffset + P.comb_bytes + 15u) & ~15u;
   if ((uint64_t)rows * P.comb_bytes >= kSendLineBytes)
     stage_rows<true>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
@@ -214,10 +145,8 @@ __global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendPara
 }
 
 hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream) {
-  const int rounds = p.num_experts <= kSendBlock ? 1 : p.num_experts <= 4 * kSendBlock ? 4 : 16;
-  const uint32_t prefix_bytes = ((uint32_t)(kSendBlock * rounds + 1) * 4u + 15u) & ~15u;
   const uint32_t msg_stride = ((uint32_t)kMsgLdsOffset + p.comb_bytes + 15u) & ~15u;
-  const size_t lds = prefix_bytes + (size_t)p.nbuf * msg_stride;
+  const size_t lds = count_prefix_bytes(p.num_experts) + (size_t)p.nbuf * msg_stride;
   combine_send_kernel<<<blocks, kSendBlock, lds, stream>>>(p);
   return hipGetLastError();
 }

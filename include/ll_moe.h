@@ -249,6 +249,55 @@ int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden
                         int max_spins, int32_t* refusal, hipStream_t stream);
 
 /*
+ * ll_moe_dispatch_recv — expert side of the dispatch of set `parity`: wait
+ * until the set's messages are complete, then unpack them into the arrays
+ * an expert's matrix product reads.
+ *   - rocSHMEM example "LL_MoE/LL_MoE_Buffers.hpp", struct LLMoEBuffer: the
+ *     receive rows [num_experts * num_tokens, hidden + 1] and the int64
+ *     per-expert count.
+ *   - mscclpp "mscclpp.h", comment above struct mscclppDevConn: the
+ *     receiver reads only after the signal.
+ *   - memra-engine "src/tp_ar.rs", memra_tp_ar_1stage: a device wait is
+ *     bounded and leaves a refusal code when it runs out.
+ * Set q is complete once its counts (the low halves of its signal words,
+ * each taken as max_tokens if larger) add up to `expected`, the number of
+ * messages the step routes (num_tokens * topk less masked entries): a
+ * partial count does not tell which of an expert's slots are written, the
+ * sum does. Then, for every expert e and j < count_e, receive row
+ * r = e * max_tokens + j gives:
+ *   payload row r := the message's payload without its header (bf16: the
+ *     2 * hidden bytes of x[t]; fp8: the hidden e4m3 codes);
+ *   scales row r  := fp8 only: its hidden / 128 fp32 scales;
+ *   src_tokens[r] := its int32 header t;
+ *   counts[e]     := count_e.
+ * Rows at or past count_e are not written; bytes move unchanged.
+ *   layout:     device, as for dispatch. Read: set q's signal words and
+ *               receive rows. Written: set 1-q's signal words (zeroed).
+ *   expected:   0 <= expected <= num_experts * max_tokens.
+ *   payload:    device, [num_experts * max_tokens, row] with row = 2*hidden
+ *               (bf16) or hidden (fp8) bytes, 16-byte aligned.
+ *   scales:     device, fp32 [num_experts * max_tokens, hidden / 128],
+ *               4-byte aligned; fp8 only (ignored for bf16, may be NULL).
+ *   src_tokens: device, int32 [num_experts * max_tokens].
+ *   counts:     device, int32 [num_experts].
+ *   max_spins:  >= 1; polls of the counts before the wait gives up.
+ *   refusal:    device, int32, zeroed by the caller; the wait running out
+ *               ORs LL_MOE_REFUSAL_COUNT_WAIT into it, and the outputs are
+ *               then unspecified. Every wait is bounded.
+ * No output may overlap the layout. The call may be enqueued on another
+ * stream before the dispatch of set q completes (it then waits for it),
+ * but after every earlier launch that cleans or reads set q. If it holds
+ * the GPU resources the dispatch needs to run, the wait runs out into a
+ * refusal. Requires num_experts <= LL_MOE_SEND_MAX_EXPERTS and
+ * num_experts * max_tokens < 2^31. Enqueued on `stream`.
+ */
+#define LL_MOE_REFUSAL_COUNT_WAIT 2
+int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
+                         int dtype, int parity, int expected, void* payload, float* scales,
+                         int32_t* src_tokens, int32_t* counts, int max_spins,
+                         int32_t* refusal, hipStream_t stream);
+
+/*
  * ll_moe_clean_signals — zero the num_experts int64 signal words of set
  * `parity` (the rocSHMEM example's clean_meta(): the dispatch count words
  * and the combine flag words are one array). Enqueued on `stream`.

@@ -158,6 +158,28 @@ def test_combine_recv_rejects_bad_arguments(case):
     assert rc == ll.INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", [
+    dict(parity=2), dict(hidden=1020), dict(dtype=7), dict(dtype=1, hidden=1000),
+    dict(layout=0), dict(layout=FAKE + 8), dict(payload=0), dict(payload=BIG + 4),
+    dict(src=0), dict(src=2 * BIG + 2), dict(counts=0), dict(counts=3 * BIG + 1),
+    dict(refusal=0), dict(refusal=4 * BIG + 2), dict(dtype=1, scales=0),
+    dict(dtype=1, scales=5 * BIG + 2), dict(expected=-1), dict(expected=8 * 128 + 1),
+    dict(max_spins=0), dict(num_experts=4097), dict(max_tokens=1 << 20, num_experts=4096),
+    dict(payload=FAKE + 64), dict(src=FAKE + 4), dict(counts=FAKE + 4),
+    dict(dtype=1, scales=FAKE + 4),
+])
+def test_dispatch_recv_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(layout=FAKE, max_tokens=128, hidden=1024, num_experts=8, dtype=0, parity=0,
+             expected=16, payload=BIG, scales=5 * BIG, src=2 * BIG, counts=3 * BIG,
+             max_spins=10, refusal=4 * BIG)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_dispatch_recv", a["layout"], a["max_tokens"], a["hidden"],
+                       a["num_experts"], a["dtype"], a["parity"], a["expected"], a["payload"],
+                       a["scales"], a["src"], a["counts"], a["max_spins"], a["refusal"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 def test_binding_routes_through_the_library_only():
     """The binding imports neither the oracle nor the workload generators."""
     src = open(os.path.join(ROOT, "combine_ll_moe_amd", "__init__.py")).read()
