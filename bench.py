@@ -55,16 +55,27 @@ def two_phase_bytes(w, md: int, routed: int) -> dict:
     return {"send": send, "recv": recv}
 
 
+def unpack_bytes(w, md: int, routed: int) -> int:
+    """Bytes the dispatch's expert side must move per launch: read the
+    counts and every received message; write the header-free payload rows
+    (and fp8 scale rows), the source tokens and the counts; clean the other
+    set's words."""
+    h, e = w.hidden, w.num_experts
+    row = 2 * h if w.dtype == 0 else h + 4 * (h // 128)
+    return 8 * e + routed * md + routed * (row + 4) + 4 * e + 8 * e
+
+
 KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
-                "send": "combine_send_kernel", "recv": "combine_recv_kernel"}
+                "send": "combine_send_kernel", "recv": "combine_recv_kernel",
+                "unpack": "dispatch_recv_kernel"}
 COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                              "hbm_counters.json")
 
 
 # The sources of the dispatch / combine path (launch shapes included); the
 # diagnostic kernels are not part of it.
-PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "kernels.h", "layout.h", "message.h",
-                "route.h", "two_phase.hip")
+PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "expert.h", "kernels.h", "layout.h",
+                "message.h", "receive.hip", "route.h", "two_phase.hip")
 
 
 def kernel_source_hash() -> str:
@@ -151,9 +162,10 @@ def summarize_profiles(args) -> None:
     md = (4 + 2 * w.hidden) if w.dtype == W.BF16 else (4 + w.hidden + w.hidden // 32)
     ab = algorithmic_bytes(w, md, w.num_tokens * w.topk)
     ab.update(two_phase_bytes(w, md, w.num_tokens * w.topk))
+    ab["unpack"] = unpack_bytes(w, md, w.num_tokens * w.topk)
     f_fetch = copy["fetch_kib"] * 1024.0 / copy["bytes"]
     f_write = copy["write_kib"] * 1024.0 / copy["bytes"]
-    lines = [f"# {args.workload}: dispatch, combine and two-phase combine kernels (rocprofv3)", "",
+    lines = [f"# {args.workload}: dispatch, combine, two-phase combine and expert-side kernels (rocprofv3)", "",
              f"Workload: {w.name}, N={w.num_tokens}, hidden={w.hidden}, experts={w.num_experts}, "
              f"top-k={w.topk}, payload {'bf16' if w.dtype == W.BF16 else 'fp8 e4m3'}.", "",
              "## Kernel durations (`--kernel-trace --stats`)", "",
@@ -177,14 +189,24 @@ def summarize_profiles(args) -> None:
               "combine back to back (roofline timing), then the two-phase warm-up steps",
               "two-phase steps (dispatch, combine_send, combine_recv), then one step preparing set 0",
               "combine_send back to back on one set, then one step preparing set 0",
-              "combine_recv back to back on one set",
-              "cold: after a 512 MiB eviction, event pairs between launches",
-              "warm, the same event pairs between launches"]
+              "combine_recv back to back on one set, then the expert-side warm-up steps",
+              "dispatch_recv back to back on one prepared set",
+              "dispatch + dispatch_recv steps on one stream"]
+    titles += ["dispatch start to expert inputs: dispatch_recv queued after the dispatch "
+               "(20 single steps)"] * 20
+    titles += ["dispatch start to expert inputs: dispatch_recv already waiting on a second "
+               "stream (20 single steps)"] * 20
+    titles += ["cold: after a 512 MiB eviction, event pairs between launches",
+               "warm, the same event pairs between launches"]
+    merged = {}
+    for title, seg in zip(titles, segs):
+        for name, ds in seg.items():
+            merged.setdefault(title, {}).setdefault(name, []).extend(ds)
     lines += ["", "## The same launches by timed region of bench.py", "",
               "Each region starts after a stream hold (a spin kernel), queued behind two "
               "signal-word cleans (not listed).", "",
               "| region | kernel | calls | average us |", "|---|---|---|---|"]
-    for title, seg in zip(titles, segs):
+    for title, seg in merged.items():
         for name, ds in seg.items():
             if "clean_kernel" in name:  # the set resets queued before each hold
                 continue
@@ -290,6 +312,8 @@ def main():
                     help="skip the plain-kernel context timings (empty launch, fill, copy)")
     ap.add_argument("--no-two-phase", action="store_true",
                     help="skip the two-phase combine timings")
+    ap.add_argument("--no-expert-side", action="store_true",
+                    help="skip the expert-side receive timings")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed after evicting L2 and MALL (0: skip)")
     ap.add_argument("--summarize-profiles", action="store_true",
@@ -520,6 +544,71 @@ def main():
         print(f"[bench] two-phase: {tp_us:.2f} us/step (send {send_us:.2f}, recv {recv_us:.2f}); "
               f"fused {ms_per_step * 1e3:.2f}", file=sys.stderr, flush=True)
 
+    # the dispatch's expert side (ll_moe_dispatch_recv): alone, K launches on
+    # one prepared set; then the latency from the dispatch's start to the
+    # unpacked expert inputs, with the receiver queued after the dispatch on
+    # the same stream, or already waiting on a second stream (overlapped)
+    expert_side = None
+    if not args.no_expert_side:
+        rows = w.num_experts * w.capacity
+        pb = 2 * w.hidden if w.dtype == W.BF16 else w.hidden
+        u_payload = torch.empty((rows, pb), dtype=torch.uint8, device=dev)
+        u_scales = (torch.empty((rows, w.hidden // 128), dtype=torch.float32, device=dev)
+                    if w.dtype == W.FP8_E4M3 else None)
+        u_src = torch.empty(rows, dtype=torch.int32, device=dev)
+        u_counts = torch.empty(w.num_experts, dtype=torch.int32, device=dev)
+        u_ref = torch.zeros(1, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream()
+
+        def unpack(s, st=None):
+            ll.ll_moe_dispatch_recv(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1,
+                                    routed[s % len(batches)], u_payload, u_scales, u_src,
+                                    u_counts, 1 << 20, u_ref, sptr if st is None else st)
+
+        reset_sets()
+        for s in range(args.warmup):
+            dispatch(s)
+            unpack(s)
+        unpack_us = time_kernel(lambda s: unpack(0), prepare=lambda: dispatch(0))
+        seq_step_us = time_kernel(lambda s: (dispatch(s), unpack(s)))
+
+        def latency(overlapped: bool, trials: int = 20):
+            out = []
+            for i in range(trials):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                reset_sets()
+                side.wait_stream(stream)  # after the reset, before the hold
+                torch.cuda._sleep(HOLD_CYCLES)
+                a.record(stream)
+                dispatch(i)
+                if overlapped:
+                    unpack(i, side.cuda_stream)
+                    b.record(side)
+                else:
+                    unpack(i)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b) * 1e3)
+            return float(np.median(out))
+
+        lat_seq = latency(False)
+        lat_ovl = latency(True)
+        torch.cuda.synchronize()
+        ub = unpack_bytes(w, md, routed[0])
+        expert_side = {
+            "unpack_us": round(unpack_us, 3),
+            "unpack_gbs": round(ub / (unpack_us * 1e-6) / 1e9, 2),
+            "bytes_per_launch": ub,
+            "sequential_steps_us": round(seq_step_us, 3),
+            "dispatch_to_inputs_us": {"same_stream": round(lat_seq, 3),
+                                      "overlapped": round(lat_ovl, 3)},
+            "refusals": int(u_ref.item()) != ll.RECV_READY,
+            "traffic": stored_traffic(w.name, "unpack")}
+        print(f"[bench] expert side: unpack {unpack_us:.2f} us; dispatch start to expert inputs "
+              f"{lat_seq:.2f} us queued after it, {lat_ovl:.2f} us overlapped",
+              file=sys.stderr, flush=True)
+
     # cold steps: the decode working set fits in the 256 MB MALL, so back to
     # back the step runs from cache; here a 512 MiB write evicts L2 and MALL
     # before every step, and event pairs time each launch. The same event
@@ -599,6 +688,7 @@ def main():
                            "min": round(min(trials), 3) if trials else None},
         "cold": cold,
         "two_phase_combine": two_phase,
+        "expert_side": expert_side,
         "floors": floors,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

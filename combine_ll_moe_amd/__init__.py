@@ -28,6 +28,7 @@ MAX_EXPERTS = 1 << 20
 SEND_MAX_EXPERTS = 4096
 REFUSAL_FLAG_WAIT = 1
 REFUSAL_COUNT_WAIT = 2
+RECV_READY = 0x100
 
 SUCCESS = 0
 HIP_ERROR = 1
@@ -137,10 +138,10 @@ def ll_moe_combine_recv(layout, max_tokens: int, num_tokens: int, hidden: int, n
 
 def ll_moe_dispatch_recv(layout, max_tokens: int, hidden: int, num_experts: int, dtype: int,
                          parity: int, expected: int, payload, scales, src_tokens, counts,
-                         max_spins: int, refusal, stream=None) -> None:
+                         max_spins: int, status, stream=None) -> None:
     _check(_lib.ll_moe_dispatch_recv(_ptr(layout), max_tokens, hidden, num_experts, dtype, parity,
                                      expected, _ptr(payload), _ptr(scales), _ptr(src_tokens),
-                                     _ptr(counts), max_spins, _ptr(refusal), _stream(stream)),
+                                     _ptr(counts), max_spins, _ptr(status), _stream(stream)),
            "ll_moe_dispatch_recv")
 
 

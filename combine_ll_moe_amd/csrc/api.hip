@@ -265,7 +265,7 @@ constexpr int kUnpackBlocks = 256;
 extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
                                     int dtype, int parity, int expected, void* payload,
                                     float* scales, int32_t* src_tokens, int32_t* counts,
-                                    int max_spins, int32_t* refusal, hipStream_t stream) {
+                                    int max_spins, int32_t* status, hipStream_t stream) {
   Layout L;
   int rc = check_shape(max_tokens, 0, hidden, num_experts, 1, dtype, parity, &L);
   if (rc != LL_MOE_SUCCESS) return rc;
@@ -275,10 +275,10 @@ extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, in
   if (slots > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
   if (expected < 0 || expected > slots || max_spins < 1) return LL_MOE_INVALID_ARGUMENT;
   if (!layout || !aligned(layout, 16)) return LL_MOE_INVALID_ARGUMENT;
-  if (!payload || !src_tokens || !counts || !refusal) return LL_MOE_INVALID_ARGUMENT;
+  if (!payload || !src_tokens || !counts || !status) return LL_MOE_INVALID_ARGUMENT;
   if (dtype == kFp8 && !scales) return LL_MOE_INVALID_ARGUMENT;
   if (!aligned(payload, 16) || !aligned(src_tokens, 4) || !aligned(counts, 4) ||
-      !aligned(refusal, 4) || (dtype == kFp8 && !aligned(scales, 4)))
+      !aligned(status, 4) || (dtype == kFp8 && !aligned(scales, 4)))
     return LL_MOE_INVALID_ARGUMENT;
   const uint64_t row_bytes = dtype == kBf16 ? 2 * (uint64_t)hidden : (uint64_t)hidden;
   // the outputs are written while the layout is read: no overlap
@@ -297,7 +297,7 @@ extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, in
   p.scales = scales;
   p.src = src_tokens;
   p.counts = counts;
-  p.refusal = refusal;
+  p.status = status;
   p.max_tokens = max_tokens;
   p.hidden = hidden;
   p.num_experts = num_experts;

@@ -85,7 +85,7 @@ struct UnpackParams {              // expert side of the dispatch
   float* scales;                   // fp8: [num_experts * max_tokens, hidden / 128]
   int32_t* src;                    // [num_experts * max_tokens] source tokens
   int32_t* counts;                 // [num_experts]
-  int32_t* refusal;                // refusal word: set when the wait runs out
+  int32_t* status;                 // zeroed by the caller: ready, or a refusal
   int max_tokens;
   int hidden;
   int num_experts;
@@ -103,6 +103,8 @@ constexpr int kSendBlock = 256;
 // of ll_moe_dispatch_recv ran out.
 constexpr int32_t kRefusalFlagWait = 1;
 constexpr int32_t kRefusalCountWait = 2;
+// Status of ll_moe_dispatch_recv: the counts added up.
+constexpr int32_t kStatusReady = 0x100;
 
 // LDS placement of a message: it starts at this offset of its buffer, so
 // that the payload (message byte 4) is 16-byte aligned; a buffer is

@@ -281,9 +281,14 @@ int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden
  *   src_tokens: device, int32 [num_experts * max_tokens].
  *   counts:     device, int32 [num_experts].
  *   max_spins:  >= 1; polls of the counts before the wait gives up.
- *   refusal:    device, int32, zeroed by the caller; the wait running out
- *               ORs LL_MOE_REFUSAL_COUNT_WAIT into it, and the outputs are
- *               then unspecified. Every wait is bounded.
+ *   status:     device, int32, 4-byte aligned, zeroed by the caller. One
+ *               workgroup polls the counts and posts the outcome here for
+ *               the others: LL_MOE_RECV_READY once the counts have added
+ *               up; LL_MOE_REFUSAL_COUNT_WAIT set when a wait ran out (the
+ *               outputs are then unspecified). Every wait is bounded.
+ * An `expected` other than the routed count is a caller error: too large,
+ * the wait runs out; too small, the unpack may start early and its outputs
+ * are unspecified (every access stays inside the arrays described here).
  * No output may overlap the layout. The call may be enqueued on another
  * stream before the dispatch of set q completes (it then waits for it),
  * but after every earlier launch that cleans or reads set q. If it holds
@@ -292,10 +297,11 @@ int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden
  * num_experts * max_tokens < 2^31. Enqueued on `stream`.
  */
 #define LL_MOE_REFUSAL_COUNT_WAIT 2
+#define LL_MOE_RECV_READY 0x100
 int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
                          int dtype, int parity, int expected, void* payload, float* scales,
                          int32_t* src_tokens, int32_t* counts, int max_spins,
-                         int32_t* refusal, hipStream_t stream);
+                         int32_t* status, hipStream_t stream);
 
 /*
  * ll_moe_clean_signals — zero the num_experts int64 signal words of set

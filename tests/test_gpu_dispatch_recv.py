@@ -39,13 +39,13 @@ class Outputs:
                                      device=DEV)
         self.src = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
         self.counts = torch.full((w.num_experts,), -7, dtype=torch.int32, device=DEV)
-        self.refusal = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.status = torch.zeros(1, dtype=torch.int32, device=DEV)
 
     def launch(self, st: Step, q, expected, max_spins=1 << 20, stream=None):
         w = st.w
         ll.ll_moe_dispatch_recv(st.lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, expected,
                                 self.payload, self.scales, self.src, self.counts, max_spins,
-                                self.refusal, stream=stream)
+                                self.status, stream=stream)
 
 
 def _check(st: Step, q, outs: Outputs, expected, filled_rows):
@@ -58,7 +58,7 @@ def _check(st: Step, q, outs: Outputs, expected, filled_rows):
     payload, scales, src, counts = oracle.dispatch_recv(
         st.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, expected, out=ref_out)
     torch.cuda.synchronize()
-    assert int(outs.refusal.item()) == 0
+    assert int(outs.status.item()) == ll.RECV_READY
     assert np.array_equal(outs.counts.cpu().numpy(), counts)
     assert np.array_equal(outs.src.cpu().numpy(), src)
     if outs.rows * outs.pb <= FULL_COMPARE_BYTES:
@@ -124,7 +124,7 @@ def test_unpack_workloads(name):
         say(f"[expert side] {name} parity {q} ok")
 
 
-@pytest.mark.parametrize("name", ["decode", "decode_fp8", "wide_zipf"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode_fp8", "wide_zipf", "worst_fill"])
 def test_unpack_beside_a_running_dispatch(name):
     w = W.WORKLOADS[name]
     x, idx = W.tokens(w), W.routing(w)
@@ -193,7 +193,7 @@ def test_refusal_when_the_counts_never_add_up(delta):
     outs = Outputs(w)
     outs.launch(st, 0, idx.size + delta, max_spins=8)
     torch.cuda.synchronize()
-    assert int(outs.refusal.item()) == ll.REFUSAL_COUNT_WAIT
+    assert int(outs.status.item()) & ll.REFUSAL_COUNT_WAIT
     with pytest.raises(oracle.CountsIncomplete):
         oracle.dispatch_recv(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, 0,
                              idx.size + delta)
