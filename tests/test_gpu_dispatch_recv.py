@@ -200,3 +200,55 @@ def test_refusal_when_the_counts_never_add_up(delta):
     st.check_signals()
     # the next step is exact again
     _step(st, 1, x, idx)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_fp8"])
+def test_unpack_graph_replays(name):
+    """dispatch + dispatch_recv for parity 0 then 1, with the status words
+    cleared by a fill kernel inside the graph, replayed three times with
+    sentinel fills between replays: every replay unpacks the same bytes."""
+    w = W.WORKLOADS[name]
+    x, idx = W.tokens(w), W.routing(w)
+    st = Step(w, full_image=False)
+    xd, idd = to_dev(x), to_dev(idx)
+    expected = int(idx.size)
+    outs = [Outputs(w) for _ in range(2)]
+    for q in (0, 1):  # eager, checked against the oracle
+        st.dispatch(q, x, idx, x_dev=xd, idx_dev=idd)
+        outs[q].launch(st, q, expected)
+        _check(st, q, outs[q], expected, _filled(w, idx))
+    refs = [(o.payload.clone(), None if o.scales is None else o.scales.clone(), o.src.clone(),
+             o.counts.clone()) for o in outs]
+    n, k = idx.shape
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            gs = torch.cuda.current_stream().cuda_stream
+            for q in (0, 1):
+                outs[q].status.zero_()
+                ll.ll_moe_dispatch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
+                                   xd, idd, gs)
+                outs[q].launch(st, q, expected, stream=gs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o in outs:  # eager work between replays
+            o.payload.fill_(SENT)
+            o.src.fill_(-7)
+            o.counts.fill_(-7)
+            o.status.fill_(5)
+            if o.scales is not None:
+                o.scales.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for q in (0, 1):
+            o, ref = outs[q], refs[q]
+            assert int(o.status.item()) == ll.RECV_READY, (r, q)
+            assert torch.equal(o.payload, ref[0]) and torch.equal(o.src, ref[2])
+            assert torch.equal(o.counts, ref[3])
+            if ref[1] is not None:
+                assert torch.equal(o.scales.view(torch.int32), ref[1].view(torch.int32))
+        say(f"[unpack graph] {name} replay {r} ok")

@@ -218,3 +218,47 @@ def test_bad_header_stages_nothing():
     st.check_staging(0, idx)
     _, refusal, _ = st.combine_recv(0, idx, wt, max_spins=16, with_oracle=False)
     assert refusal == ll.REFUSAL_FLAG_WAIT
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_two_phase_graph_replays(name):
+    """Two two-phase steps (parity 0, then 1) captured into a HIP graph with
+    the refusal words cleared by a fill kernel inside it, replayed three
+    times with eager work between replays: every replay gives the eager
+    bits and no refusal."""
+    w = W.WORKLOADS[name]
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    xd, idd, wtd, yd = to_dev(x), to_dev(idx), to_dev(wt), to_dev(y)
+    refs = [_two_phase_step(st, q, x, idx, wt, y, yd) for q in (0, 1)]
+    n, k = idx.shape
+    outs = [torch.empty((n, w.hidden), dtype=torch.float32, device=DEV) for _ in range(2)]
+    refusals = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(2)]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            gs = torch.cuda.current_stream().cuda_stream
+            for q in (0, 1):
+                refusals[q].zero_()
+                ll.ll_moe_dispatch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
+                                   xd, idd, gs)
+                ll.ll_moe_combine_send(st.lay, w.capacity, w.hidden, w.num_experts, w.dtype, q,
+                                       yd, gs)
+                ll.ll_moe_combine_recv(st.lay, w.capacity, n, w.hidden, w.num_experts, k,
+                                       w.dtype, q, idd, wtd, outs[q], 1 << 20, refusals[q], gs)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for q in (0, 1):  # eager work between replays
+            outs[q].fill_(float("nan"))
+            refusals[q].fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for q in (0, 1):
+            assert int(refusals[q].item()) == 0, (r, q)
+            got = outs[q].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), refs[q].view(np.uint32)), (r, q)
+        say(f"[two-phase graph] {name} replay {r} ok")
