@@ -262,3 +262,19 @@ def test_two_phase_graph_replays(name):
             got = outs[q].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), refs[q].view(np.uint32)), (r, q)
         say(f"[two-phase graph] {name} replay {r} ok")
+
+
+def test_two_phase_masked_entries():
+    """Entries outside [0, num_experts) are not dispatched, not staged and
+    not folded; the other picks of the same tokens still are."""
+    w = W.Workload("masked", 64, 1024, 16, 4, W.BF16, "uniform", seed=13)
+    x, idx, wt = W.tokens(w), W.routing(w), W.weights(w)
+    idx[3, 1] = -1
+    idx[10, 0] = w.num_experts
+    idx[40, 3] = -5
+    idx[41] = -1  # a token with no routed pick: its output row is all +0
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        out = _two_phase_step(st, q, x, idx, wt, y)
+        assert (out[41].view(np.uint32) == 0).all()
