@@ -502,32 +502,44 @@ def main():
     # flags counting past the counts; the token side re-folds raised flags)
     two_phase = None
     if not args.no_two_phase:
-        refusal = torch.zeros(1, dtype=torch.int32, device=dev)
+        # one caller-zeroed status word per token-side call
+        nwords = max(args.steps, args.warmup) + 1
+        tp_status = torch.zeros(nwords, dtype=torch.int32, device=dev)
         spins = 1 << 20
 
         def send(s):
             ll.ll_moe_combine_send(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1, y,
                                    sptr)
 
-        def recv(s):
+        def recv(s, word):
             _, idx, wt = batches[s % len(batches)]
             ll.ll_moe_combine_recv(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
-                                   w.topk, w.dtype, s & 1, idx, wt, out, spins, refusal, sptr)
+                                   w.topk, w.dtype, s & 1, idx, wt, out, spins,
+                                   tp_status[word:word + 1], sptr)
 
-        def tp_step(s):
+        def tp_step(s, word=None):
             dispatch(s)
             send(s)
-            recv(s)
+            recv(s, s if word is None else word)
+
+        def prepared_set0():
+            tp_status.zero_()
+            tp_step(0, nwords - 1)  # set 0: one step's counts and flags
+
+        def all_ready(n):
+            torch.cuda.synchronize()
+            return bool((tp_status[:n] == ll.RECV_READY).all().item())
 
         reset_sets()
+        tp_status.zero_()
         for s in range(args.warmup):
             tp_step(s)
-        tp_us = time_kernel(tp_step)
-        tp_ok = int(refusal.item()) == 0
-        # set 0 prepared after the region's reset: one step's counts and flags
-        send_us = time_kernel(lambda s: send(0), prepare=lambda: tp_step(0))
-        recv_us = time_kernel(lambda s: recv(0), prepare=lambda: tp_step(0))
-        tp_ok = tp_ok and int(refusal.item()) == 0
+        tp_ok = all_ready(args.warmup)
+        tp_us = time_kernel(tp_step, prepare=tp_status.zero_)
+        tp_ok = tp_ok and all_ready(args.steps)
+        send_us = time_kernel(lambda s: send(0), prepare=prepared_set0)
+        recv_us = time_kernel(lambda s: recv(0, s), prepare=prepared_set0)
+        tp_ok = tp_ok and all_ready(args.steps)
         for q in (0, 1):
             ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q)
         torch.cuda.synchronize()
@@ -557,40 +569,59 @@ def main():
                     if w.dtype == W.FP8_E4M3 else None)
         u_src = torch.empty(rows, dtype=torch.int32, device=dev)
         u_counts = torch.empty(w.num_experts, dtype=torch.int32, device=dev)
-        u_ref = torch.zeros(1, dtype=torch.int32, device=dev)
+        # one caller-zeroed status word per call
+        u_nwords = max(args.steps, args.warmup) + 1
+        u_status = torch.zeros(u_nwords, dtype=torch.int32, device=dev)
         side = torch.cuda.Stream()
+        u_ok = True
 
-        def unpack(s, st=None):
+        def unpack(s, word, st=None):
             ll.ll_moe_dispatch_recv(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1,
                                     routed[s % len(batches)], u_payload, u_scales, u_src,
-                                    u_counts, 1 << 20, u_ref, sptr if st is None else st)
+                                    u_counts, 1 << 20, u_status[word:word + 1],
+                                    sptr if st is None else st)
+
+        def u_ready(n):
+            torch.cuda.synchronize()
+            return bool((u_status[:n] == ll.RECV_READY).all().item())
+
+        def u_prepare():
+            u_status.zero_()
+            dispatch(0)
 
         reset_sets()
+        u_status.zero_()
         for s in range(args.warmup):
             dispatch(s)
-            unpack(s)
-        unpack_us = time_kernel(lambda s: unpack(0), prepare=lambda: dispatch(0))
-        seq_step_us = time_kernel(lambda s: (dispatch(s), unpack(s)))
+            unpack(s, s)
+        u_ok = u_ready(args.warmup)
+        unpack_us = time_kernel(lambda s: unpack(0, s), prepare=u_prepare)
+        u_ok = u_ok and u_ready(args.steps)
+        seq_step_us = time_kernel(lambda s: (dispatch(s), unpack(s, s)), prepare=u_status.zero_)
+        u_ok = u_ok and u_ready(args.steps)
 
         def latency(overlapped: bool, trials: int = 20):
-            out = []
+            nonlocal u_ok
+            res = []
             for i in range(trials):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
                 reset_sets()
-                side.wait_stream(stream)  # after the reset, before the hold
+                u_status.zero_()
+                side.wait_stream(stream)  # after the reset and the zeroing, before the hold
                 torch.cuda._sleep(HOLD_CYCLES)
                 a.record(stream)
                 dispatch(i)
                 if overlapped:
-                    unpack(i, side.cuda_stream)
+                    unpack(i, 0, side.cuda_stream)
                     b.record(side)
                 else:
-                    unpack(i)
+                    unpack(i, 0)
                     b.record(stream)
                 torch.cuda.synchronize()
-                out.append(a.elapsed_time(b) * 1e3)
-            return float(np.median(out))
+                u_ok = u_ok and u_ready(1)
+                res.append(a.elapsed_time(b) * 1e3)
+            return float(np.median(res))
 
         lat_seq = latency(False)
         lat_ovl = latency(True)
@@ -603,7 +634,7 @@ def main():
             "sequential_steps_us": round(seq_step_us, 3),
             "dispatch_to_inputs_us": {"same_stream": round(lat_seq, 3),
                                       "overlapped": round(lat_ovl, 3)},
-            "refusals": int(u_ref.item()) != ll.RECV_READY,
+            "refusals": not u_ok,
             "traffic": stored_traffic(w.name, "unpack")}
         print(f"[bench] expert side: unpack {unpack_us:.2f} us; dispatch start to expert inputs "
               f"{lat_seq:.2f} us queued after it, {lat_ovl:.2f} us overlapped",

@@ -129,10 +129,10 @@ def ll_moe_combine_send(layout, max_tokens: int, hidden: int, num_experts: int, 
 
 def ll_moe_combine_recv(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
                         topk: int, dtype: int, parity: int, topk_idx, topk_weights, out,
-                        max_spins: int, refusal, stream=None) -> None:
+                        max_spins: int, status, stream=None) -> None:
     _check(_lib.ll_moe_combine_recv(_ptr(layout), max_tokens, num_tokens, hidden, num_experts,
                                     topk, dtype, parity, _ptr(topk_idx), _ptr(topk_weights),
-                                    _ptr(out), max_spins, _ptr(refusal), _stream(stream)),
+                                    _ptr(out), max_spins, _ptr(status), _stream(stream)),
            "ll_moe_combine_recv")
 
 

@@ -217,17 +217,17 @@ extern "C" int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int
 extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden,
                                    int num_experts, int topk, int dtype, int parity,
                                    const int32_t* topk_idx, const float* topk_weights, float* out,
-                                   int max_spins, int32_t* refusal, hipStream_t stream) {
+                                   int max_spins, int32_t* status, hipStream_t stream) {
   Layout L;
   int rc = check_shape(max_tokens, num_tokens, hidden, num_experts, topk, dtype, parity, &L);
   if (rc != LL_MOE_SUCCESS) return rc;
   rc = check_two_phase(L, hidden, num_experts, max_tokens, layout);
   if (rc != LL_MOE_SUCCESS) return rc;
   if (max_spins < 1) return LL_MOE_INVALID_ARGUMENT;
+  if (!status || !aligned(status, 4)) return LL_MOE_INVALID_ARGUMENT;
   if (num_tokens > 0) {
-    if (!topk_idx || !topk_weights || !out || !refusal) return LL_MOE_INVALID_ARGUMENT;
-    if (!aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
-        !aligned(refusal, 4))
+    if (!topk_idx || !topk_weights || !out) return LL_MOE_INVALID_ARGUMENT;
+    if (!aligned(out, 16) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4))
       return LL_MOE_INVALID_ARGUMENT;
     // out may not overlap the layout whose staging rows it folds
     if (overlaps(layout, L.total, out, (uint64_t)num_tokens * hidden * 4))
@@ -242,7 +242,7 @@ extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens,
   p.idx = topk_idx;
   p.w = topk_weights;
   p.out = reinterpret_cast<float4*>(out);
-  p.refusal = refusal;
+  p.status = status;
   p.num_tokens = num_tokens;
   p.max_tokens = max_tokens;
   p.hidden = hidden;

@@ -64,7 +64,7 @@ struct RecvParams {                // two-phase combine, token side
   const int32_t* idx;              // int32 [num_tokens, topk]
   const float* w;                  // fp32 [num_tokens, topk]
   float4* out;                     // fp32 [num_tokens, hidden]
-  int32_t* refusal;                // refusal word: set when a flag wait runs out
+  int32_t* status;                 // zeroed by the caller: ready, or a refusal
   int num_tokens;
   int max_tokens;
   int hidden;
@@ -99,11 +99,15 @@ struct UnpackParams {              // expert side of the dispatch
 // The two-phase combine's expert side keeps every expert's count in LDS.
 constexpr int kSendMaxExperts = 4096;
 constexpr int kSendBlock = 256;
+// The two-phase combine's token side: at most this many workgroups (two per
+// CU), looping over its work items.
+constexpr int kRecvBlocks = 512;
 // Refusal codes: a flag wait of ll_moe_combine_recv ran out; the count wait
 // of ll_moe_dispatch_recv ran out.
 constexpr int32_t kRefusalFlagWait = 1;
 constexpr int32_t kRefusalCountWait = 2;
-// Status of ll_moe_dispatch_recv: the counts added up.
+// Status of ll_moe_dispatch_recv and ll_moe_combine_recv: the wait ended
+// well (the counts added up; every flag came up).
 constexpr int32_t kStatusReady = 0x100;
 
 // LDS placement of a message: it starts at this offset of its buffer, so

@@ -190,6 +190,7 @@ int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int hidden,
  */
 #define LL_MOE_SEND_MAX_EXPERTS 4096
 #define LL_MOE_REFUSAL_FLAG_WAIT 1
+#define LL_MOE_RECV_READY 0x100
 
 /*
  * ll_moe_combine_send — expert side: stage every received message's output
@@ -218,8 +219,8 @@ int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int num_expert
                         hipStream_t stream);
 
 /*
- * ll_moe_combine_recv — token side: wait for the flag of every routed
- * expert of a token, then fold the staged rows.
+ * ll_moe_combine_recv — token side: wait for the experts' flags, then fold
+ * the staged rows.
  *   layout:       device, as for dispatch. Read: set q's signal words and
  *                 staging rows. Written: set 1-q's signal words (zeroed).
  *   topk_idx:     device, int32 [num_tokens, topk] (the dispatch routing;
@@ -227,26 +228,27 @@ int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int num_expert
  *   topk_weights: device, fp32 [num_tokens, topk].
  *   out:          device, fp32 [num_tokens, hidden], 16-byte aligned; may
  *                 not overlap the layout.
- *   max_spins:    >= 1; polls of one flag before its wait gives up.
- *   refusal:      device, int32, 4-byte aligned, zeroed by the caller
- *                 (may be NULL when num_tokens is 0).
+ *   max_spins:    >= 1; polls of the flags before the wait gives up.
+ *   status:       device, int32, 4-byte aligned, zeroed by the caller. One
+ *                 workgroup polls the flags and posts the outcome here for
+ *                 the others: LL_MOE_RECV_READY once every expert's flag is
+ *                 up (an expert that received nothing is up);
+ *                 LL_MOE_REFUSAL_FLAG_WAIT set when a wait ran out, and out
+ *                 is then unspecified. Every wait is bounded, so the launch
+ *                 always ends.
  * out[t, c] = fma chain over the routed k in ascending order, from +0.0f,
  * of acc = fmaf(w[t, k], bf16 column c of staging row e * max_tokens + t,
  * acc), in fp32: the same expression, and so the same bits, as
  * ll_moe_combine on the same routing and expert outputs.
- * A wait that runs out ORs LL_MOE_REFUSAL_FLAG_WAIT into *refusal, and
- * out is then unspecified (rows of that token, and of later tokens that the
- * same workgroup serves, may be left unwritten); every wait is bounded, so
- * the launch always ends. Order: after the dispatch of set q (its counts must
- * be final); it may run at the same time as ll_moe_combine_send of set q on
- * another stream and then waits for its flags (if it holds the GPU resources
- * the expert side needs to start, the waits run out into a refusal).
- * Enqueued on `stream`.
+ * Order: after the dispatch of set q (its counts must be final); it may be
+ * enqueued on another stream before ll_moe_combine_send of set q runs and
+ * then waits for its flags (its grid is bounded, 512 workgroups, so that it
+ * leaves the expert side room to run). Enqueued on `stream`.
  */
 int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden,
                         int num_experts, int topk, int dtype, int parity,
                         const int32_t* topk_idx, const float* topk_weights, float* out,
-                        int max_spins, int32_t* refusal, hipStream_t stream);
+                        int max_spins, int32_t* status, hipStream_t stream);
 
 /*
  * ll_moe_dispatch_recv — expert side of the dispatch of set `parity`: wait
@@ -297,7 +299,6 @@ int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden
  * num_experts * max_tokens < 2^31. Enqueued on `stream`.
  */
 #define LL_MOE_REFUSAL_COUNT_WAIT 2
-#define LL_MOE_RECV_READY 0x100
 int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
                          int dtype, int parity, int expected, void* payload, float* scales,
                          int32_t* src_tokens, int32_t* counts, int max_spins,

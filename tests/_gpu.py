@@ -96,21 +96,21 @@ class Step:
     def combine_recv(self, q, idx: np.ndarray, wt: np.ndarray, max_spins=1 << 22, stream=None,
                      with_oracle=True):
         """Token side on the GPU (and the oracle's, unless with_oracle is
-        False); returns (out, refusal word, oracle out or None) once the
-        GPU is done."""
+        False); returns (out, status word, oracle out or None) once the GPU
+        is done."""
         w = self.w
         n = idx.shape[0]
         out = torch.full((n, w.hidden), float("nan"), dtype=torch.float32, device=DEV)
-        refusal = torch.zeros(1, dtype=torch.int32, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
         ll.ll_moe_combine_recv(self.lay, w.capacity, n, w.hidden, w.num_experts, idx.shape[1],
-                               w.dtype, q, to_dev(idx), to_dev(wt), out, max_spins, refusal,
+                               w.dtype, q, to_dev(idx), to_dev(wt), out, max_spins, status,
                                stream=stream)
         ref = None
         if with_oracle:
             ref = oracle.combine_recv(self.img, w.capacity, w.hidden, w.num_experts, w.dtype, q,
                                       idx, wt)
         torch.cuda.synchronize()
-        return out.cpu().numpy(), int(refusal.item()), ref
+        return out.cpu().numpy(), int(status.item()), ref
 
     def check_staging(self, q, idx: np.ndarray):
         """Set q's staging rows of every routed (t, k) against the oracle,

@@ -145,16 +145,16 @@ def test_combine_send_rejects_bad_arguments(case):
     dict(hidden=1020), dict(hidden=22528), dict(num_experts=4097, topk=2), dict(layout=0),
     dict(layout=FAKE + 4), dict(idx=0), dict(idx=BIG + 2), dict(w=0), dict(w=BIG + 1),
     dict(out=0), dict(out=2 * BIG + 4), dict(out=FAKE + 64), dict(max_spins=0),
-    dict(max_spins=-5), dict(refusal=0), dict(refusal=3 * BIG + 2),
+    dict(max_spins=-5), dict(status=0), dict(status=3 * BIG + 2), dict(status=0, num_tokens=0),
 ])
 def test_combine_recv_rejects_bad_arguments(case):
     import combine_ll_moe_amd as ll
     a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
-             dtype=0, parity=0, idx=BIG, w=BIG, out=2 * BIG, max_spins=100, refusal=3 * BIG)
+             dtype=0, parity=0, idx=BIG, w=BIG, out=2 * BIG, max_spins=100, status=3 * BIG)
     a.update(case)
     rc = ll.raw_status("ll_moe_combine_recv", a["layout"], a["max_tokens"], a["num_tokens"],
                        a["hidden"], a["num_experts"], a["topk"], a["dtype"], a["parity"],
-                       a["idx"], a["w"], a["out"], a["max_spins"], a["refusal"], None)
+                       a["idx"], a["w"], a["out"], a["max_spins"], a["status"], None)
     assert rc == ll.INVALID_ARGUMENT
 
 
@@ -162,7 +162,7 @@ def test_combine_recv_rejects_bad_arguments(case):
     dict(parity=2), dict(hidden=1020), dict(dtype=7), dict(dtype=1, hidden=1000),
     dict(layout=0), dict(layout=FAKE + 8), dict(payload=0), dict(payload=BIG + 4),
     dict(src=0), dict(src=2 * BIG + 2), dict(counts=0), dict(counts=3 * BIG + 1),
-    dict(refusal=0), dict(refusal=4 * BIG + 2), dict(dtype=1, scales=0),
+    dict(status=0), dict(status=4 * BIG + 2), dict(dtype=1, scales=0),
     dict(dtype=1, scales=5 * BIG + 2), dict(expected=-1), dict(expected=8 * 128 + 1),
     dict(max_spins=0), dict(num_experts=4097), dict(max_tokens=1 << 20, num_experts=4096),
     dict(payload=FAKE + 64), dict(src=FAKE + 4), dict(counts=FAKE + 4),
@@ -172,11 +172,11 @@ def test_dispatch_recv_rejects_bad_arguments(case):
     import combine_ll_moe_amd as ll
     a = dict(layout=FAKE, max_tokens=128, hidden=1024, num_experts=8, dtype=0, parity=0,
              expected=16, payload=BIG, scales=5 * BIG, src=2 * BIG, counts=3 * BIG,
-             max_spins=10, refusal=4 * BIG)
+             max_spins=10, status=4 * BIG)
     a.update(case)
     rc = ll.raw_status("ll_moe_dispatch_recv", a["layout"], a["max_tokens"], a["hidden"],
                        a["num_experts"], a["dtype"], a["parity"], a["expected"], a["payload"],
-                       a["scales"], a["src"], a["counts"], a["max_spins"], a["refusal"], None)
+                       a["scales"], a["src"], a["counts"], a["max_spins"], a["status"], None)
     assert rc == ll.INVALID_ARGUMENT
 
 

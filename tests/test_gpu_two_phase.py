@@ -33,8 +33,8 @@ def _two_phase_step(st: Step, q, x, idx, wt, y, y_dev=None):
     st.check_dispatch(q, idx, restore=False)
     st.combine_send(q, y, y_dev)
     st.check_staging(q, idx)
-    out, refusal, ref = st.combine_recv(q, idx, wt)
-    assert refusal == 0, f"refusal word {refusal}"
+    out, status, ref = st.combine_recv(q, idx, wt)
+    assert status == ll.RECV_READY, f"status word {status:#x}"
     st.check_signals()
     diff = check_combine(out, ref)
     assert diff == 0, f"{diff} outputs differ in bits"
@@ -108,7 +108,7 @@ def test_two_phase_decode_steps():
     say("[two-phase] decode 20 steps ok")
 
 
-@pytest.mark.parametrize("name", ["decode", "wide_zipf"])
+@pytest.mark.parametrize("name", ["decode", "wide_zipf", "worst_fill"])
 def test_token_side_waits_for_the_flags(name):
     """The token side is launched on its own stream right after the dispatch,
     while the expert side is held back on the main stream: it has to wait
@@ -124,18 +124,18 @@ def test_token_side_waits_for_the_flags(name):
         side = torch.cuda.Stream()
         side.wait_stream(main)  # the dispatch is complete before the wait starts
         out = torch.full((n, w.hidden), float("nan"), dtype=torch.float32, device=DEV)
-        refusal = torch.zeros(1, dtype=torch.int32, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
         # expert side first (held), so that a shared hardware queue would run
         # it before the waiting token side instead of behind it
         torch.cuda._sleep(HOLD_CYCLES)
         ll.ll_moe_combine_send(st.lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, yd,
                                stream=main)
         ll.ll_moe_combine_recv(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
-                               idd, wd, out, 1 << 22, refusal, stream=side)
+                               idd, wd, out, 1 << 22, status, stream=side)
         oracle.combine_send(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, y)
         ref = oracle.combine_recv(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, idx, wt)
         torch.cuda.synchronize()
-        assert int(refusal.item()) == 0
+        assert int(status.item()) == ll.RECV_READY
         assert check_combine(out.cpu().numpy(), ref) == 0
         st.check_staging(q, idx)
         say(f"[two-phase] {name} concurrent parity {q} ok")
@@ -143,7 +143,7 @@ def test_token_side_waits_for_the_flags(name):
 
 def test_refusal_without_expert_side():
     """No expert side: every wait runs out after max_spins polls and the
-    refusal word says so; the launch ends, the other set's words are zeroed,
+    status word says so; the launch ends, the other set's words are zeroed,
     and a normal step afterwards is exact."""
     w = W.WORKLOADS["tiny"]
     x, idx, wt, y = _inputs(w)
@@ -152,8 +152,8 @@ def test_refusal_without_expert_side():
     st.check_dispatch(0, idx, restore=False)
     with pytest.raises(oracle.FlagNotRaised):
         oracle.combine_recv(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, 0, idx, wt)
-    _, refusal, _ = st.combine_recv(0, idx, wt, max_spins=16, with_oracle=False)
-    assert refusal == ll.REFUSAL_FLAG_WAIT
+    _, status, _ = st.combine_recv(0, idx, wt, max_spins=16, with_oracle=False)
+    assert status & ll.REFUSAL_FLAG_WAIT
     st.check_signals()
     _two_phase_step(st, 1, x, idx, wt, y)
 
@@ -174,8 +174,8 @@ def test_refusal_on_a_short_flag():
     st.img[off:off + 8].view(np.int64)[0] += 1
     with pytest.raises(oracle.FlagNotRaised):
         oracle.combine_recv(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, 1, idx, wt)
-    _, refusal, _ = st.combine_recv(1, idx, wt, max_spins=16, with_oracle=False)
-    assert refusal == ll.REFUSAL_FLAG_WAIT
+    _, status, _ = st.combine_recv(1, idx, wt, max_spins=16, with_oracle=False)
+    assert status & ll.REFUSAL_FLAG_WAIT
 
 
 def test_bad_header_stages_nothing():
@@ -216,16 +216,16 @@ def test_bad_header_stages_nothing():
         sig[ex] = counts[ex] | (staged << 32)
     torch.cuda.synchronize()
     st.check_staging(0, idx)
-    _, refusal, _ = st.combine_recv(0, idx, wt, max_spins=16, with_oracle=False)
-    assert refusal == ll.REFUSAL_FLAG_WAIT
+    _, status, _ = st.combine_recv(0, idx, wt, max_spins=16, with_oracle=False)
+    assert status & ll.REFUSAL_FLAG_WAIT
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
 def test_two_phase_graph_replays(name):
     """Two two-phase steps (parity 0, then 1) captured into a HIP graph with
-    the refusal words cleared by a fill kernel inside it, replayed three
+    the status words cleared by a fill kernel inside it, replayed three
     times with eager work between replays: every replay gives the eager
-    bits and no refusal."""
+    bits and a ready status."""
     w = W.WORKLOADS[name]
     x, idx, wt, y = _inputs(w)
     st = Step(w, full_image=False)
@@ -233,7 +233,7 @@ def test_two_phase_graph_replays(name):
     refs = [_two_phase_step(st, q, x, idx, wt, y, yd) for q in (0, 1)]
     n, k = idx.shape
     outs = [torch.empty((n, w.hidden), dtype=torch.float32, device=DEV) for _ in range(2)]
-    refusals = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(2)]
+    statuses = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in range(2)]
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -242,23 +242,23 @@ def test_two_phase_graph_replays(name):
         with torch.cuda.graph(g, stream=side):
             gs = torch.cuda.current_stream().cuda_stream
             for q in (0, 1):
-                refusals[q].zero_()
+                statuses[q].zero_()
                 ll.ll_moe_dispatch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q,
                                    xd, idd, gs)
                 ll.ll_moe_combine_send(st.lay, w.capacity, w.hidden, w.num_experts, w.dtype, q,
                                        yd, gs)
                 ll.ll_moe_combine_recv(st.lay, w.capacity, n, w.hidden, w.num_experts, k,
-                                       w.dtype, q, idd, wtd, outs[q], 1 << 20, refusals[q], gs)
+                                       w.dtype, q, idd, wtd, outs[q], 1 << 20, statuses[q], gs)
     torch.cuda.synchronize()
     for r in range(3):
         for q in (0, 1):  # eager work between replays
             outs[q].fill_(float("nan"))
-            refusals[q].fill_(7)
+            statuses[q].fill_(7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for q in (0, 1):
-            assert int(refusals[q].item()) == 0, (r, q)
+            assert int(statuses[q].item()) == ll.RECV_READY, (r, q)
             got = outs[q].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), refs[q].view(np.uint32)), (r, q)
         say(f"[two-phase graph] {name} replay {r} ok")
