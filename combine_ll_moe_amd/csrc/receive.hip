@@ -16,8 +16,9 @@
 // the dispatch. Workgroup 0 polls the counts with relaxed device-scope
 // loads and scans them in LDS until their sum reaches the expected number,
 // at most max_spins times, and posts the outcome in a status word the
-// caller zeroed; the other workgroups poll that one word, then scan the
-// (now final) counts themselves. Each takes a contiguous run of the
+// caller zeroed; every other workgroup looks at the counts once itself and,
+// if they do not add up yet, polls that one word, then scans the (now
+// final) counts. Each takes a contiguous run of the
 // flattened (expert, slot) rows; each wavefront copies whole rows, so that a row's buffer descriptor
 // is uniform and its payload can be read with device-coherent (sc1) loads.
 // Those loads are served at device scope, like the polls, and issue after
@@ -67,9 +68,11 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
       __hip_atomic_fetch_or(P.status, ready ? kStatusReady : kRefusalCountWait, __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
     if (!ready) return;
-  } else {
-    // a follower waits at most twice as many rounds as workgroup 0 polls,
-    // its rounds being shorter
+  } else if (load_count_prefix(P.sig, E, P.max_tokens, pre, wave_sum) != (uint32_t)P.expected) {
+    // A follower looks at the counts once itself (queued after the dispatch
+    // they are final, and it need not wait for workgroup 0's post); if they
+    // do not add up yet it polls the status word, at most twice as many
+    // rounds as workgroup 0 polls, its rounds being shorter.
     const int limit = P.max_spins > (1 << 29) ? (1 << 30) : 2 * P.max_spins + 64;
     for (int spins = 1;; ++spins) {
       if (tid == 0) {
@@ -88,7 +91,7 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
       if (v & kStatusReady) break;
       __builtin_amdgcn_s_sleep(2);
     }
-    // the counts are final: workgroup 0 saw them add up before posting
+    // the counts are final now: workgroup 0 saw them add up before posting
     load_count_prefix(P.sig, E, P.max_tokens, pre, wave_sum);
   }
   const uint32_t rows = pre[kSendBlock * count_rounds(E)];

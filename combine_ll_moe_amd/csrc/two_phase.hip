@@ -30,9 +30,9 @@
 //    atomic on the word's high half.
 //  - Token side. Workgroup 0 polls every expert's flag (relaxed
 //    device-scope loads, at most max_spins rounds) and posts the outcome in
-//    a caller-zeroed status word that the other workgroups poll, so that
-//    the waiting adds almost no traffic to the signal words the expert side
-//    is raising. Then work items of (tile of tokens, run of columns), as the
+//    a caller-zeroed status word; every other workgroup looks at the flags
+//    once and, if some are down, polls that one word, so that the waiting
+//    adds almost no traffic to the signal words the expert side is raising. Then work items of (tile of tokens, run of columns), as the
 //    fused combine but with no routing prologue (a token's staging row for
 //    pick k is e * max_tokens + t), over a grid of at most kRecvBlocks
 //    workgroups that leaves a not-yet-started expert side room to run: the
@@ -254,9 +254,18 @@ __global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvP
                             __HIP_MEMORY_SCOPE_AGENT);
     if (!up) return;
   } else {
-    // a follower waits at most twice as many rounds as workgroup 0 polls
-    const int limit = P.max_spins > (1 << 29) ? (1 << 30) : 2 * P.max_spins + 64;
-    for (int spins = 1;; ++spins) {
+    // A follower looks at the flags once itself (queued after the expert
+    // side they are up, and it need not wait for workgroup 0's post); if
+    // some are down it polls the status word, at most twice as many rounds
+    // as workgroup 0 polls.
+    bool pending = false;
+    for (int e = tid; e < E; e += blockDim.x) {
+      const uint64_t s = __hip_atomic_load(P.sig + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pending = pending || (uint32_t)(s >> 32) != (uint32_t)s;
+    }
+    const int limit = !__syncthreads_or(pending) ? 0
+                      : P.max_spins > (1 << 29) ? (1 << 30) : 2 * P.max_spins + 64;
+    for (int spins = 1; limit > 0; ++spins) {
       if (tid == 0) {
         int32_t v = __hip_atomic_load(P.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (v == 0 && spins >= limit) {
