@@ -21,13 +21,20 @@ namespace {
 // once there are enough workgroups to give each of the 256 CUs about two.
 constexpr int kTargetBlocks = 512;
 constexpr int kMaxTileTokens = 2;
+// The dispatch keeps one token per workgroup up to twice as many
+// workgroups: a batch of 1024 tokens of 7168 columns dispatches 7% faster
+// with 1024 one-token workgroups (four resident per CU) than with 512
+// two-token ones, whose second message waits behind the first.
+constexpr int kDispatchTileBlocks = 1024;
 constexpr uint64_t kStreamRowsBytes = 64ull << 20;
 // LDS a dispatch workgroup may use for message buffers: 64 KiB less the
-// routing prologue's static share.
-constexpr uint32_t kDispatchLdsBudget = 65536 - (uint32_t)sizeof(RouteShared);
+// routing prologue's share (its tile entries and its histogram).
+uint32_t dispatch_lds_budget(int num_experts) {
+  return 65536u - (uint32_t)sizeof(RouteShared) - 4u * (uint32_t)hist_cap_for(num_experts);
+}
 
-int tile_for(int num_tokens, int per_token_blocks, int topk) {
-  int tile = (int)(((int64_t)num_tokens * per_token_blocks) / kTargetBlocks);
+int tile_for(int num_tokens, int per_token_blocks, int topk, int target = kTargetBlocks) {
+  int tile = (int)(((int64_t)num_tokens * per_token_blocks) / target);
   if (tile > kMaxTileTokens) tile = kMaxTileTokens;
   if (tile > kMaxTileEntries / topk) tile = kMaxTileEntries / topk;
   return tile < 1 ? 1 : tile;
@@ -103,10 +110,11 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   if (groups > topk + 1) groups = topk + 1;
   if (groups < 1) groups = 1;
   p.groups = groups;
-  p.tile = tile_for(num_tokens, groups, topk);
+  p.tile = tile_for(num_tokens, groups, topk, kDispatchTileBlocks);
   p.msg_bytes = (uint32_t)L.dispatch_msg;
   p.msg_stride = ((uint32_t)kMsgLdsOffset + p.msg_bytes + 15u) & ~15u;
-  p.nbuf = 2 * p.msg_stride <= kDispatchLdsBudget ? 2 : 1;
+  // a second message buffer only serves a tile of several tokens
+  p.nbuf = p.tile > 1 && 2 * p.msg_stride <= dispatch_lds_budget(num_experts) ? 2 : 1;
   // Large dispatches write mostly to HBM, where whole-line stores pay off;
   // smaller ones stay in L2 and MALL, where the plain mapping is a little
   // faster (3% at 16 MB, 24% the other way at 132 MB).

@@ -89,6 +89,7 @@ __device__ __forceinline__ void combine_token(const CombineParams& P, const Rout
 template <int MAXK, bool STREAM>
 __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombineParams P) {
   __shared__ RouteShared rs;
+  extern __shared__ int hist[];  // hist_cap_for(num_experts) ints
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
     for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
@@ -100,7 +101,8 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   if (t0 >= P.num_tokens) return;
   const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
 
-  route_tile(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs);
+  route_tile(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs, hist,
+             hist_cap_for(P.num_experts));
 
   const int chunks = P.hidden / 8;
   const int c = sl * blockDim.x + tid;
@@ -110,14 +112,15 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
 
 template <bool STREAM>
 static void launch_k(const CombineParams& p, int blocks, hipStream_t stream) {
+  const size_t lds = sizeof(int) * hist_cap_for(p.num_experts);
   if (p.topk <= 2)
-    combine_kernel<2, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_kernel<2, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
   else if (p.topk <= 4)
-    combine_kernel<4, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_kernel<4, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
   else if (p.topk <= 8)
-    combine_kernel<8, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_kernel<8, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
   else
-    combine_kernel<16, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_kernel<16, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {

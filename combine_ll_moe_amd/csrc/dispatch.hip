@@ -293,6 +293,7 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   u32x4 r[kStage];
   route_tile(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
+      reinterpret_cast<int*>(lds_raw + P.nbuf * P.msg_stride), hist_cap_for(P.num_experts),
       [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
       [&]() {
         build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
@@ -362,7 +363,7 @@ static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   // whole rounds of kXcds tiles, so that the index mapping covers every tile
   const int rounds = (tiles + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)p.nbuf * p.msg_stride;
+  const size_t lds = (size_t)p.nbuf * p.msg_stride + sizeof(int) * hist_cap_for(p.num_experts);
   dispatch_kernel<DT, LINE><<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }

@@ -14,8 +14,10 @@
 // L2):
 //   slot(j) = (entries before the tile naming e)      an LDS histogram
 //           + (tile entries before j naming e)        a rank in registers
-// The histogram covers kHistExperts experts per pass; more experts take
-// more passes over the earlier entries. Loads are unconditional (indices
+// The histogram lives in the caller's LDS and covers hist_cap experts per
+// pass (min(num_experts, kHistExperts), sized at launch, so a small expert
+// count leaves LDS to other workgroups); more experts take more passes over
+// the earlier entries. Loads are unconditional (indices
 // clamped into the table, clamped lanes masked afterwards), so the compiler
 // issues them back to back.
 #pragma once
@@ -33,10 +35,14 @@ constexpr int kWave = 64;
 constexpr int kHistExperts = 4096;
 constexpr int kMaxTileEntries = kWave;  // tokens per tile * topk: one wavefront's lanes
 
+// Histogram entries of the routing prologue for num_experts experts.
+__host__ __device__ constexpr int hist_cap_for(int num_experts) {
+  return num_experts < kHistExperts ? (num_experts > 0 ? num_experts : 1) : kHistExperts;
+}
+
 struct RouteShared {
   int expert[kMaxTileEntries];  // idx of the tile's entries, tile order
   int slot[kMaxTileEntries];    // their slots, or -1 when masked
-  int hist[kHistExperts];
 };
 
 // Number of lanes below this one in its 16-lane row (DPP row) whose v
@@ -79,7 +85,8 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 
 // All threads of the workgroup must call this (it contains barriers).
 // On return rs.expert[j] and rs.slot[j] hold entry j = (t - t0) * topk + k
-// of the tile for t0 <= t < t1. Requires (t1 - t0) * topk <= kMaxTileEntries.
+// of the tile for t0 <= t < t1. Requires (t1 - t0) * topk <= kMaxTileEntries;
+// hist is an LDS array of hist_cap >= 1 ints.
 //
 // Every global load of the first pass (the tile's own entries and the first
 // round of earlier entries) is issued before anything waits on one, so the
@@ -98,7 +105,8 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 template <typename Issue = NoOverlap, typename Overlap = NoOverlap, typename Ready = NoOverlap>
 __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
-                                           RouteShared& rs, const Issue& issue = Issue(),
+                                           RouteShared& rs, int* hist, int hist_cap,
+                                           const Issue& issue = Issue(),
                                            const Overlap& overlap = Overlap(),
                                            const Ready& ready = Ready()) {
   const int tid = threadIdx.x;
@@ -133,8 +141,8 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
   int rank = 0;  // wavefront 0: earlier lanes holding the same expert
   auto pass = [&](int c0, auto first_pass) {
     constexpr bool kFirst = decltype(first_pass)::value;
-    const int width = num_experts - c0 < kHistExperts ? num_experts - c0 : kHistExperts;
-    for (int i = tid; i < width; i += nthreads) rs.hist[i] = 0;
+    const int width = num_experts - c0 < hist_cap ? num_experts - c0 : hist_cap;
+    for (int i = tid; i < width; i += nthreads) hist[i] = 0;
     __syncthreads();
     for (int it = 0; it < rounds; ++it) {
       const int base = it * stride + tid;
@@ -153,7 +161,7 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
       for (int u = 0; u < kUnroll; ++u) {
         const int p = base + u * nthreads;
         const unsigned rel = (unsigned)v[u] - (unsigned)c0;
-        if (p < first && rel < (unsigned)width) atomicAdd(&rs.hist[rel], 1);
+        if (p < first && rel < (unsigned)width) atomicAdd(&hist[rel], 1);
       }
     }
     if constexpr (kFirst) {
@@ -177,14 +185,14 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
     if (tid < kWave) {
       const unsigned rel = (unsigned)mine - (unsigned)c0;
       if (tid < n && rel < (unsigned)width) {
-        const int s = rs.hist[rel] + rank;
+        const int s = hist[rel] + rank;
         rs.slot[tid] = s < max_tokens ? s : -1;
       }
     }
     __syncthreads();
   };
   pass(0, std::true_type{});
-  for (int c0 = kHistExperts; c0 < num_experts; c0 += kHistExperts)  // uniform
+  for (int c0 = hist_cap; c0 < num_experts; c0 += hist_cap)  // uniform
     pass(c0, std::false_type{});
 }
 
