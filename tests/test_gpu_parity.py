@@ -141,18 +141,23 @@ def test_masked_repeated_and_overflowing_picks():
 
 @pytest.mark.parametrize("shape", [
     # (N, Nmax, h, E, K, dtype): messages near the 45056-byte limit leave LDS
-    # room for one message buffer; the N=1024 cases take two-token tiles
-    # (the single buffer is reused with a barrier) and whole-line stores;
-    # fp8 at h=43648 quantizes in six batches of four rounds
+    # room for one message buffer; the N=1024 cases take one-token tiles and
+    # whole-line stores, the N=2048 cases two-token tiles (the dispatch grows
+    # tiles past 1024 workgroups; the single buffer is reused with a
+    # barrier); fp8 at h=43648 quantizes in six batches of four rounds
     (64, 64, 22520, 16, 4, W.BF16),
     (1024, 1024, 22520, 16, 2, W.BF16),
+    (2048, 2048, 22520, 16, 2, W.BF16),
     (32, 32, 43648, 8, 2, W.FP8_E4M3),
     (1024, 1024, 43648, 8, 2, W.FP8_E4M3),
+    (2048, 2048, 43648, 8, 2, W.FP8_E4M3),
 ])
 def test_largest_messages(shape):
     n, cap, h, e, k, dt = shape
     md, _ = oracle.message_bytes(h, dt)
-    assert 2 * (((12 + md) + 15) // 16 * 16) > 65536 - 18432 and md <= ll.MAX_MESSAGE_BYTES
+    # LDS of a dispatch workgroup: 64 KiB less the tile entries (512 B) and
+    # the histogram (4 bytes per expert): no room for a second buffer
+    assert 2 * (((12 + md) + 15) // 16 * 16) > 65536 - 512 - 4 * e and md <= ll.MAX_MESSAGE_BYTES
     say(f"[parity] largest messages: N={n} h={h} E={e} K={k} dtype={dt} md={md}")
     w = W.Workload("big", n, h, e, k, dt, "uniform", max_tokens=cap, seed=h + n)
     x, idx, wt, y = _inputs(w)
@@ -162,12 +167,14 @@ def test_largest_messages(shape):
 
 
 @pytest.mark.parametrize("shape", [
-    # (N, E, K): one-token tiles of 8 entries (DPP-row ranks), and two-token
-    # tiles of 32 entries (the register walk); experts drawn with
-    # replacement, so tokens repeat experts, plus masked entries and
-    # experts that overflow their capacity
+    # (N, E, K): one-token tiles of 8 and 16 entries (DPP-row ranks), and
+    # two-token tiles of 32 entries (the register walk: the combine's at
+    # N=1024, the dispatch's at N=2048); experts drawn with replacement, so
+    # tokens repeat experts, plus masked entries and experts that overflow
+    # their capacity
     (64, 8, 8),
     (1024, 32, 16),
+    (2048, 32, 16),
 ])
 def test_repeated_picks_in_every_rank_path(shape):
     n, e, k = shape
