@@ -79,15 +79,20 @@ PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "expert.h", "kernels.h
 
 
 def kernel_source_hash() -> str:
-    """Hash of the path's HIP sources; stored counters apply only to the same code."""
+    """Hash of the path's HIP sources with comments and blank space taken
+    out; stored counters apply only to the same code."""
     import hashlib
+    import re
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_ll_moe_amd", "csrc")
     h = hashlib.sha256()
     for name in PATH_SOURCES:
         f = os.path.join(root, name)
         h.update(name.encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

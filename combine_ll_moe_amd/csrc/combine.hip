@@ -13,9 +13,8 @@
 // Design on gfx950: one workgroup per (tile of consecutive tokens, run of
 // columns). It computes the tile's slots once (route.h); then, token by
 // token, every thread issues its topk 16-byte loads of bf16 expert rows at
-// once (all outstanding together, and the next token's requested before the
-// current one is reduced), folds them with v_fma_f32 in k order, and writes
-// 8 fp32 results as two 16-byte stores. Workgroup 0 zeroes the other set's
+// once (all outstanding together), folds them with v_fma_f32 in k order,
+// and writes 8 fp32 results as two 16-byte streaming stores. Workgroup 0 zeroes the other set's
 // signal words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
