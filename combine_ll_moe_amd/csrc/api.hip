@@ -33,6 +33,20 @@ uint32_t dispatch_lds_budget(int num_experts) {
   return 65536u - (uint32_t)sizeof(RouteShared) - 4u * (uint32_t)hist_cap_for(num_experts);
 }
 
+// The dispatch's routing prologue reads the table 4 entries per load when
+// the entries before the last tile would take more than two rounds of
+// single-entry loads (2048 entries each), the table is 16-byte aligned and
+// it is a whole number of 4-entry vectors: a late tile's later load rounds
+// otherwise queue behind the other workgroups' message stores (worst-fill:
+// prologues of up to 9 us; dispatch 28.9 -> 28.0 us). The combine keeps
+// single-entry loads: its length is set by its gather either way.
+constexpr int64_t kWideIdxEntries = 4096;
+
+int wide_idx_for(const int32_t* idx, int num_tokens, int topk) {
+  const int64_t entries = (int64_t)num_tokens * topk;
+  return entries > kWideIdxEntries && entries % 4 == 0 && ((uintptr_t)idx & 15) == 0;
+}
+
 int tile_for(int num_tokens, int per_token_blocks, int topk, int target = kTargetBlocks) {
   int tile = (int)(((int64_t)num_tokens * per_token_blocks) / target);
   if (tile > kMaxTileTokens) tile = kMaxTileTokens;
@@ -119,6 +133,7 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   // smaller ones stay in L2 and MALL, where the plain mapping is a little
   // faster (3% at 16 MB, 24% the other way at 132 MB).
   p.line_align = (uint64_t)num_tokens * (uint64_t)(topk + 1) * L.dispatch_msg >= kStreamRowsBytes;
+  p.wide_idx = wide_idx_for(topk_idx, num_tokens, topk);
   return from_hip(launch_dispatch(p, dtype, stream));
 }
 

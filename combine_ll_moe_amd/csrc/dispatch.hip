@@ -257,7 +257,7 @@ __device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* 
   }
 }
 
-template <int DT, bool LINE>
+template <int DT, bool LINE, int VEC>
 __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const DispatchParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ RouteShared rs;
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   //    message is complete, while wavefront 0 ranks the slots.
   constexpr int kStage = 4;
   u32x4 r[kStage];
-  route_tile(
+  route_tile<VEC>(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
       reinterpret_cast<int*>(lds_raw + P.nbuf * P.msg_stride), hist_cap_for(P.num_experts),
       [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
@@ -358,20 +358,25 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   }
 }
 
-template <int DT, bool LINE>
+template <int DT, bool LINE, int VEC>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   // whole rounds of kXcds tiles, so that the index mapping covers every tile
   const int rounds = (tiles + kXcds - 1) / kXcds;
   const size_t lds = (size_t)p.nbuf * p.msg_stride + sizeof(int) * hist_cap_for(p.num_experts);
-  dispatch_kernel<DT, LINE><<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
+  dispatch_kernel<DT, LINE, VEC><<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }
 
+template <int DT>
+static hipError_t launch_lines(const DispatchParams& p, hipStream_t stream) {
+  if (p.line_align)
+    return p.wide_idx ? launch_dt<DT, true, 4>(p, stream) : launch_dt<DT, true, 1>(p, stream);
+  return p.wide_idx ? launch_dt<DT, false, 4>(p, stream) : launch_dt<DT, false, 1>(p, stream);
+}
+
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream) {
-  if (dtype == kBf16)
-    return p.line_align ? launch_dt<kBf16, true>(p, stream) : launch_dt<kBf16, false>(p, stream);
-  return p.line_align ? launch_dt<kFp8, true>(p, stream) : launch_dt<kFp8, false>(p, stream);
+  return dtype == kBf16 ? launch_lines<kBf16>(p, stream) : launch_lines<kFp8>(p, stream);
 }
 
 // The fp8 encoder above, applied element-wise in groups of four; lets a test

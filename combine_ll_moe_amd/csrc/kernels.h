@@ -25,6 +25,7 @@ struct DispatchParams {
   uint32_t msg_stride;             // bytes of one LDS message buffer
   int nbuf;                        // LDS message buffers (2: double-buffered)
   int line_align;                  // deal store chunks to lanes by whole cache lines
+  int wide_idx;                    // routing prologue reads 4 entries per load
 };
 
 struct CombineParams {

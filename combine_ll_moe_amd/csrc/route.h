@@ -19,7 +19,11 @@
 // count leaves LDS to other workgroups); more experts take more passes over
 // the earlier entries. Loads are unconditional (indices
 // clamped into the table, clamped lanes masked afterwards), so the compiler
-// issues them back to back.
+// issues them back to back. A round of loads covers 8 loads per thread of
+// VEC consecutive entries each: VEC = 4 (16-byte loads, for large tables
+// that are 16-byte aligned and a whole number of 4-entry vectors) covers
+// 8192 entries per round of a 256-thread workgroup, so a batch of 1024
+// tokens of 8 picks needs one load round trip instead of four.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -63,6 +67,20 @@ struct NoOverlap {
   __device__ void operator()() const {}
 };
 
+// VEC consecutive entries of the routing table, read by one load.
+template <int VEC>
+struct IdxVec;
+template <>
+struct IdxVec<1> {
+  typedef int32_t type;
+  __device__ static int at(type v, int) { return v; }
+};
+template <>
+struct IdxVec<4> {
+  typedef int32_t type __attribute__((ext_vector_type(4)));
+  __device__ static int at(type v, int j) { return v[j]; }
+};
+
 // Mask of the lanes below this one in its wavefront.
 __device__ __forceinline__ uint64_t lanes_below() {
   return (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
@@ -102,7 +120,12 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 // expert. The tile's entries sit in wavefront 0's lanes. For 4-16 entries
 // (one DPP row) the rank is 15 row shifts and compares, with no dependent
 // loop; otherwise a register walk over the earlier lanes (shorter for 1-3).
-template <typename Issue = NoOverlap, typename Overlap = NoOverlap, typename Ready = NoOverlap>
+//
+// VEC = 4 requires idx to be 16-byte aligned and the table (num_tokens *
+// topk entries) to be a multiple of 4 entries long: every vector that holds
+// an entry before the tile then lies wholly inside the table.
+template <int VEC = 1, typename Issue = NoOverlap, typename Overlap = NoOverlap,
+          typename Ready = NoOverlap>
 __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
                                            RouteShared& rs, int* hist, int hist_cap,
@@ -114,20 +137,22 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
   const int first = t0 * topk;         // entries before the tile: [0, first)
   const int n = (t1 - t0) * topk;      // the tile's entries: [first, first + n)
   constexpr int kUnroll = 8;
-  const int stride = nthreads * kUnroll;
+  typedef typename IdxVec<VEC>::type Vec;
+  const Vec* tab = reinterpret_cast<const Vec*>(idx);
+  const int stride = nthreads * kUnroll * VEC;  // entries per round
   // at least one round: the first round's loads are then consumed on every
   // path, so nothing later has to wait for them behind its own stores
   const int rounds = first > stride ? (first + stride - 1) / stride : 1;  // uniform
-  const int last = first > 0 ? first - 1 : 0;
+  const int last = first > 0 ? (first - 1) / VEC : 0;  // the load holding entry first - 1
 
   // loads of the first round and of the tile's own entries (threads j < n;
   // for a tile of up to 64 entries they stay in wavefront 0's registers);
   // indices are clamped into the table so the loads are unconditional
-  int v0[kUnroll];
+  Vec v0[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const int p = tid + u * nthreads;
-    v0[u] = idx[p < last ? p : last];
+    const int q = tid + u * nthreads;
+    v0[u] = tab[q < last ? q : last];
   }
   const int own = idx[first + (tid < n ? tid : 0)];
   issue();
@@ -145,23 +170,26 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
     for (int i = tid; i < width; i += nthreads) hist[i] = 0;
     __syncthreads();
     for (int it = 0; it < rounds; ++it) {
-      const int base = it * stride + tid;
-      int v[kUnroll];
+      const int base = it * (stride / VEC) + tid;  // in loads
+      Vec v[kUnroll];
       if (kFirst && it == 0) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) v[u] = v0[u];
       } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-          const int p = base + u * nthreads;
-          v[u] = idx[p < last ? p : last];
+          const int q = base + u * nthreads;
+          v[u] = tab[q < last ? q : last];
         }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int p = base + u * nthreads;
-        const unsigned rel = (unsigned)v[u] - (unsigned)c0;
-        if (p < first && rel < (unsigned)width) atomicAdd(&hist[rel], 1);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          const int p = (base + u * nthreads) * VEC + j;
+          const unsigned rel = (unsigned)IdxVec<VEC>::at(v[u], j) - (unsigned)c0;
+          if (p < first && rel < (unsigned)width) atomicAdd(&hist[rel], 1);
+        }
       }
     }
     if constexpr (kFirst) {
