@@ -166,24 +166,25 @@ def test_largest_messages(shape):
         _run_step(st, q, x, idx, wt, y)
 
 
-@pytest.mark.parametrize("n,k,shift", [
-    (1024, 8, 0),   # 8192 entries, 16-byte aligned: four entries per load
-    (1024, 8, 1),   # the same table 4 bytes off 16-byte alignment: one per load
-    (1025, 5, 0),   # 5125 entries, not a whole number of 4-entry loads
-    (3000, 4, 0),   # 12000 entries: two rounds of four-entry loads
+@pytest.mark.parametrize("n,k,e,shift", [
+    (1024, 8, 64, 0),    # 8192 entries, 16-byte aligned: four entries per load
+    (1024, 8, 64, 1),    # the same table 4 bytes off 16-byte alignment: one per load
+    (1025, 5, 64, 0),    # 5125 entries, not a whole number of 4-entry loads
+    (3000, 4, 64, 0),    # 12000 entries: two rounds of four-entry loads
+    (1024, 8, 5000, 0),  # four-entry loads in both histogram passes (5000 experts)
 ])
-def test_routing_table_load_widths(n, k, shift):
+def test_routing_table_load_widths(n, k, e, shift):
     """The dispatch reads a long routing table four entries per load only
     when it is 16-byte aligned and a multiple of 4 entries long; every case
     must route exactly as the oracle does."""
-    w = W.Workload("tab", n, 64, 64, k, W.BF16, "hotset", seed=n + k + shift)
+    w = W.Workload("tab", n, 64, e, k, W.BF16, "hotset", seed=n + k + shift)
     x, idx, wt, y = _inputs(w)
     buf = torch.zeros(idx.size + 4, dtype=torch.int32, device=DEV)
     idx_dev = buf[shift:shift + idx.size].view(n, k)
     idx_dev.copy_(torch.from_numpy(idx))
     assert (idx_dev.data_ptr() % 16 == 0) == (shift == 0)
-    say(f"[parity] routing table widths: N={n} K={k} shift={4 * shift} bytes")
-    st = Step(w, full_image=True)
+    say(f"[parity] routing table widths: N={n} K={k} E={e} shift={4 * shift} bytes")
+    st = Step(w, full_image=e <= 64)
     for q in (0, 1):
         st.dispatch(q, x, idx, idx_dev=idx_dev)
         st.check_dispatch(q, idx)
