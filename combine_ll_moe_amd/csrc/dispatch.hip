@@ -288,10 +288,12 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   // 1. the routing prologue; the loads of x[t0] go out with its first
   //    loads, and message(t0) is built in LDS once they are back. The send
   //    row needs no slot: this group's part of it goes out as soon as the
-  //    message is complete, while wavefront 0 ranks the slots.
+  //    message is complete; then every wavefront ranks its own copy of the
+  //    tile's slots and goes on to its receive rows without waiting for
+  //    the others.
   constexpr int kStage = 4;
   u32x4 r[kStage];
-  route_tile<VEC>(
+  const int wslot = route_tile<VEC, true>(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
       reinterpret_cast<int*>(lds_raw + P.nbuf * P.msg_stride), hist_cap_for(P.num_experts),
       [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
@@ -315,7 +317,9 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
     }
     if (t + 1 < t1) load_row<kStage>(r, x + (size_t)(t + 1) * chunks, chunks);
     for (int m = g; m < K; m += P.groups) {
-      const int s = rs.slot[i * K + m];
+      // this wavefront's own copy of the slot; the expert was in LDS before
+      // the prologue's last barrier
+      const int s = __builtin_amdgcn_readlane(wslot, i * K + m);
       if (s < 0) continue;
       copy_message<LINE>(
           P.recv + ((uint64_t)rs.expert[i * K + m] * (uint64_t)P.max_tokens + (uint64_t)s) * md, msg, md);

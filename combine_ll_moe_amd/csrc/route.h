@@ -124,9 +124,16 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 // VEC = 4 requires idx to be 16-byte aligned and the table (num_tokens *
 // topk entries) to be a multiple of 4 entries long: every vector that holds
 // an entry before the tile then lies wholly inside the table.
-template <int VEC = 1, typename Issue = NoOverlap, typename Overlap = NoOverlap,
-          typename Ready = NoOverlap>
-__device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int t0, int t1,
+//
+// WAVE_SLOTS: every wavefront holds the tile's entries in its lanes 0..n-1
+// and computes their slots itself, returned in those lanes (-1 when
+// masked), so that no barrier follows the slot computation when one
+// histogram pass covers the experts; rs.slot is still written (by
+// wavefront 0) and is visible after the caller's next barrier. Otherwise
+// the return value is meaningless and rs.slot is visible on return.
+template <int VEC = 1, bool WAVE_SLOTS = false, typename Issue = NoOverlap,
+          typename Overlap = NoOverlap, typename Ready = NoOverlap>
+__device__ __forceinline__ int route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
                                            RouteShared& rs, int* hist, int hist_cap,
                                            const Issue& issue = Issue(),
@@ -154,16 +161,21 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
     const int q = tid + u * nthreads;
     v0[u] = tab[q < last ? q : last];
   }
-  const int own = idx[first + (tid < n ? tid : 0)];
+  // the tile's own entries: in wavefront 0's lanes (WAVE_SLOTS: every
+  // wavefront's) 0..n-1
+  const int lane = WAVE_SLOTS ? (tid & (kWave - 1)) : tid;
+  const int own = idx[first + (lane < n ? lane : 0)];
   issue();
-  const int mine = tid < n ? own : -1;
+  const int mine = lane < n ? own : -1;
 
   // One histogram pass over experts [c0, c0 + width). The first pass is a
   // separate instance (first_pass is a compile-time flag) that also runs
   // the callbacks and ranks the tile, so that they run on every path
   // through it: no load they consume can look in flight afterwards, which
   // would make a later wait cover the stores issued in between.
-  int rank = 0;  // wavefront 0: earlier lanes holding the same expert
+  int rank = 0;  // wavefront 0 (WAVE_SLOTS: all): earlier lanes holding the same expert
+  int wslot = -1;  // WAVE_SLOTS: lane j's slot
+  const bool multi_pass = num_experts > hist_cap;  // uniform
   auto pass = [&](int c0, auto first_pass) {
     constexpr bool kFirst = decltype(first_pass)::value;
     const int width = num_experts - c0 < hist_cap ? num_experts - c0 : hist_cap;
@@ -202,26 +214,29 @@ __device__ __forceinline__ void route_tile(const int32_t* __restrict__ idx, int 
     __syncthreads();
     if constexpr (kFirst) {
       ready();
-      if (tid < kWave) {
+      if (WAVE_SLOTS || tid < kWave) {
         if (n > 3 && n <= 16)  // uniform
           rank = same_below_in_row<1>(mine);
         else
           for (int j = 0; j < n; ++j)
-            rank += (j < tid) & (__builtin_amdgcn_readlane(mine, j) == mine);
+            rank += (j < lane) & (__builtin_amdgcn_readlane(mine, j) == mine);
       }
     }
-    if (tid < kWave) {
+    if (WAVE_SLOTS || tid < kWave) {
       const unsigned rel = (unsigned)mine - (unsigned)c0;
-      if (tid < n && rel < (unsigned)width) {
+      if (lane < n && rel < (unsigned)width) {
         const int s = hist[rel] + rank;
-        rs.slot[tid] = s < max_tokens ? s : -1;
+        wslot = s < max_tokens ? s : -1;
+        if (tid < kWave) rs.slot[tid] = wslot;
       }
     }
-    __syncthreads();
+    // the next pass clears hist: every wavefront must be done reading it
+    if (!WAVE_SLOTS || multi_pass) __syncthreads();
   };
   pass(0, std::true_type{});
   for (int c0 = hist_cap; c0 < num_experts; c0 += hist_cap)  // uniform
     pass(c0, std::false_type{});
+  return wslot;
 }
 
 }  // namespace llmoe
