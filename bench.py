@@ -78,12 +78,13 @@ PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "expert.h", "kernels.h
                 "message.h", "receive.hip", "route.h", "two_phase.hip")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(root: str = None) -> str:
     """Hash of the path's HIP sources with comments and blank space taken
     out; stored counters apply only to the same code."""
     import hashlib
     import re
-    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_ll_moe_amd", "csrc")
+    if root is None:
+        root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "combine_ll_moe_amd", "csrc")
     h = hashlib.sha256()
     for name in PATH_SOURCES:
         f = os.path.join(root, name)
