@@ -353,7 +353,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the step has no multi-GPU path in this build)", file=sys.stderr)
+              "(the step has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch

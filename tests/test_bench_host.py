@@ -33,3 +33,13 @@ def test_source_hash_sees_code_changes(tmp_path):
     f.write_text(text.replace("constexpr int kTargetBlocks = 512;", "constexpr int kTargetBlocks = 513;"))
     assert bench.kernel_source_hash(str(dst)) != bench.kernel_source_hash(root)
 
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "measures one GPU" in r.stderr
