@@ -1,11 +1,21 @@
 """Benchmark of the low-latency MoE dispatch + combine step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload decode]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME]
 
 A step is one dispatch(q) + one combine(q) over one decode micro-batch, with
-the parity q alternating step by step, all inputs resident in HBM. The
-default workload is the decode micro-batch (128 tokens, hidden 7168, 256
-experts, top-8, bf16). Prints one JSON line on stdout:
+the parity q alternating step by step, all inputs resident in HBM.
+
+With no --workload the run times three workloads in one process, one after
+the other, each layout freed before the next is allocated:
+
+  worst_fill   1024 tokens, hidden 7168, 256 experts, top-8, bf16, half the
+               tokens on a hot set of 8 experts: the worst-case decode batch
+               the layout is sized for, and the headline;
+  decode       128 tokens, hidden 7168, 256 experts, top-8, bf16;
+  decode_fp8   as decode with the fp8 e4m3 dispatch payload.
+
+It prints one JSON line on stdout. The top-level figures are the headline
+workload's; "configs" holds the same block for every workload timed:
 
   value      effective HBM GB/s of the whole step: algorithmic bytes per step
              (what the method must move, see algorithmic_bytes()) over the
@@ -13,7 +23,13 @@ experts, top-8, bf16). Prints one JSON line on stdout:
   roofline   the dominant kernel's algorithmic bytes per launch over its
              average launch time (HIP events on its stream), against the
              8 TB/s HBM peak;
-  cpu_baseline  the CPU oracle on the same workload, single-threaded.
+  cold       the same launches after a 1 GiB read pass has evicted L2 and
+             the MALL (clean lines only: no write-back overlaps them);
+  floors     hand-written probes timed like the step: the dispatch's stores
+             alone over its exact destination rows and the combine's gather
+             alone over its exact rows, neither with routing or publish;
+  ceilings   contiguous 1 GiB write / read / copy by hand-written kernels;
+  cpu_baseline  the CPU oracle on the headline workload, one host core.
 """
 import argparse
 import json
@@ -25,7 +41,11 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 HOLD_CYCLES = 5_000_000
-COLD_EVICT_BYTES = 512 << 20  # twice the MI355X's 256 MB MALL
+# read (not written) before every cold step: four times the 256 MB MALL
+COLD_EVICT_BYTES = 1 << 30
+CEILING_BYTES = 1 << 30
+HEADLINE = "worst_fill"
+DEFAULT_WORKLOADS = ("worst_fill", "decode", "decode_fp8")
 
 
 def algorithmic_bytes(w, md: int, routed: int) -> dict:
@@ -70,12 +90,13 @@ KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
                 "unpack": "dispatch_recv_kernel"}
 COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                              "hbm_counters.json")
+COPY_KERNEL = "stream_kernel"  # the hand-written copy that calibrates the counters
 
 
 # The sources of the dispatch / combine path (launch shapes included); the
 # diagnostic kernels are not part of it.
-PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "expert.h", "kernels.h", "layout.h",
-                "message.h", "receive.hip", "route.h", "two_phase.hip")
+PATH_SOURCES = ("api.hip", "combine.hip", "dispatch.hip", "expert.h", "gather.h", "kernels.h",
+                "layout.h", "message.h", "receive.hip", "route.h", "two_phase.hip")
 
 
 def kernel_source_hash(root: str = None) -> str:
@@ -128,25 +149,52 @@ def _counter_means(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def _bench_line(log_path: str) -> dict:
+    """The JSON line a bench run printed (its log)."""
+    with open(log_path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    raise ValueError(f"{log_path}: no bench line")
+
+
+def _refusals(block: dict) -> list:
+    """Names of the waiting legs of a bench block that reported a refusal."""
+    bad = []
+    for leg in ("two_phase_combine", "expert_side"):
+        if (block.get(leg) or {}).get("refusals"):
+            bad.append(leg)
+    return bad
+
+
 def summarize_profiles(args) -> None:
     """Turn rocprofv3 CSV output into the committed summaries under profiles/:
-    a markdown table per workload and the counters file bench.py reads."""
+    a markdown table per workload and the counters file bench.py reads.
+    Counter runs whose bench line reported a refusal (a waiting kernel that
+    gave up moves none of its bytes) are not written."""
     import csv
     prof = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
     os.makedirs(prof, exist_ok=True)
+    for log in (args.fetch_log, args.write_log):
+        if log:
+            bad = _refusals(_bench_line(log))
+            if bad:
+                raise SystemExit(f"{log}: the counter run reported refusals in {bad}; "
+                                 "its counters would average launches that moved nothing")
     stats = list(csv.DictReader(open(args.trace)))
     fetch = _counter_means(args.fetch, "FETCH_SIZE")
     write = _counter_means(args.write, "WRITE_SIZE")
     cfetch = _counter_means(args.copy_fetch, "FETCH_SIZE")
     cwrite = _counter_means(args.copy_write, "WRITE_SIZE")
-    copies = [k for k in cwrite if "copy" in k.lower()]  # the probe's copy kernel
+    copies = [k for k in cwrite if COPY_KERNEL in k]
     copy_name = max(copies, key=lambda k: cwrite[k])
     copy = {"bytes": args.copy_bytes, "kernel": copy_name,
             "fetch_kib": round(cfetch[copy_name], 1), "write_kib": round(cwrite[copy_name], 1)}
     per = {}
     for short, name in KERNEL_NAMES.items():
-        fk = [k for k in fetch if name in k]
-        wk = [k for k in write if name in k]
+        fk = [k for k in fetch if name in k and "probe" not in k]
+        wk = [k for k in write if name in k and "probe" not in k]
         if fk and wk:
             per[short] = {"kernel": fk[0], "fetch_kib": round(fetch[fk[0]], 1),
                           "write_kib": round(write[wk[0]], 1)}
@@ -180,8 +228,9 @@ def summarize_profiles(args) -> None:
         lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     # the same launches split by bench.py's timed regions: each region starts
-    # with the stream hold (a spin kernel), then steps, dispatch-only and
-    # combine-only loops follow one another
+    # with the stream hold (a spin kernel); the bench line of the traced run
+    # lists the regions in order
+    titles = _bench_line(args.trace_log).get("profile_regions", [])
     trace = list(csv.DictReader(open(args.trace.replace("kernel_stats", "kernel_trace"))))
     segs, cur = [], None
     for r in trace:
@@ -191,19 +240,9 @@ def summarize_profiles(args) -> None:
         elif cur is not None:
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             cur.setdefault(r["Kernel_Name"], []).append(d)
-    titles = ["dispatch + combine steps", "dispatch back to back (roofline timing)",
-              "combine back to back (roofline timing), then the two-phase warm-up steps",
-              "two-phase steps (dispatch, combine_send, combine_recv), then one step preparing set 0",
-              "combine_send back to back on one set, then one step preparing set 0",
-              "combine_recv back to back on one set, then the expert-side warm-up steps",
-              "dispatch_recv back to back on one prepared set",
-              "dispatch + dispatch_recv steps on one stream"]
-    titles += ["dispatch start to expert inputs: dispatch_recv queued after the dispatch "
-               "(20 single steps)"] * 20
-    titles += ["dispatch start to expert inputs: dispatch_recv already waiting on a second "
-               "stream (20 single steps)"] * 20
-    titles += ["cold: after a 512 MiB eviction, event pairs between launches",
-               "warm, the same event pairs between launches"]
+    if len(titles) != len(segs):
+        raise SystemExit(f"{len(segs)} holds in the trace but {len(titles)} regions in the bench "
+                         "line: not the same run")
     merged = {}
     for title, seg in zip(titles, segs):
         for name, ds in seg.items():
@@ -218,9 +257,11 @@ def summarize_profiles(args) -> None:
                 continue
             lines.append(f"| {title} | `{name[:60]}` | {len(ds)} | {sum(ds) / len(ds):.2f} |")
     lines += ["", "## HBM bytes per launch (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`)", "",
-              f"Calibration: a plain {copy['bytes']} B device copy (`{copy_name[:60]}`) read "
+              f"Calibration: a hand-written {copy['bytes']} B device copy (`{copy_name[:60]}`) read "
               f"FETCH_SIZE {copy['fetch_kib']} KiB and WRITE_SIZE {copy['write_kib']} KiB, "
-              f"factors {f_fetch:.3f} and {f_write:.3f}.", "",
+              f"factors {f_fetch:.3f} and {f_write:.3f}. The counter runs skip the "
+              "overlapped-latency legs and reported no refusal, so every launch averaged "
+              "moved its bytes.", "",
               "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|"]
     for short, k in per.items():
@@ -234,32 +275,503 @@ def summarize_profiles(args) -> None:
     print(out)
 
 
-def floor_probes(torch, stream, hold_stream, steps: int, write_bytes: int, move_bytes: int):
-    """Context for the roofline: torch's own kernels timed back to back the
-    way the step is: an empty launch, a fill writing as many bytes as the
-    dispatch writes, and a device copy moving as many bytes as the dispatch
-    moves (half read, half written)."""
-    dev = torch.device("cuda:0")
-    buf = torch.empty(write_bytes, dtype=torch.uint8, device=dev)
-    src = torch.empty(move_bytes // 2, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
+def slot_rows(idx: np.ndarray, num_experts: int, capacity: int) -> np.ndarray:
+    """Expert-output / receive row e * capacity + slot of every pick, for the
+    floor probes only (every pick routed, at most capacity per expert): slots
+    in ascending (token, k) order per expert, by a stable sort."""
+    flat = idx.ravel().astype(np.int64)
+    assert ((flat >= 0) & (flat < num_experts)).all()
+    order = np.argsort(flat, kind="stable")
+    se = flat[order]
+    start = np.searchsorted(se, se, side="left")
+    slot = np.empty_like(flat)
+    slot[order] = np.arange(flat.size) - start
+    assert slot.max(initial=0) < capacity
+    return (flat * capacity + slot).reshape(idx.shape)
 
-    def timed(fn):
-        for _ in range(5):
-            fn()
+
+class Clock:
+    """Times GPU work on one stream. A short spin kernel first holds the
+    stream while the timed launches are queued behind it, so the events time
+    the GPU running them back to back, not the host's launch rate. Every
+    hold is preceded by `reset` (the signal-word cleans) and recorded under
+    a region name, in order, for the profile summaries."""
+
+    def __init__(self, torch, stream, reset):
+        self.torch, self.stream, self.reset = torch, stream, reset
+        self.regions = []
+
+    def hold(self, region: str, prepare=None):
+        self.reset()
+        if prepare is not None:
+            prepare()
+        self.torch.cuda._sleep(HOLD_CYCLES)
+        self.regions.append(region)
+
+    def per_call(self, region: str, fn, count: int, prepare=None) -> float:
+        """Average microseconds of fn(s), s = 0..count-1, back to back."""
+        torch = self.torch
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        hold_stream()
-        a.record(stream)
-        for _ in range(steps):
-            fn()
-        b.record(stream)
+        self.hold(region, prepare)
+        a.record(self.stream)
+        for s in range(count):
+            fn(s)
+        b.record(self.stream)
         torch.cuda.synchronize()
-        return round(a.elapsed_time(b) * 1e3 / steps, 3)
+        return a.elapsed_time(b) * 1e3 / count
 
-    return {"empty_launch_us": timed(lambda: torch.cuda._sleep(0)),
-            "fill_us": timed(lambda: buf.fill_(7)), "fill_bytes": write_bytes,
-            "copy_us": timed(lambda: dst.copy_(src)), "copy_bytes": 2 * (move_bytes // 2)}
+
+def ceilings(torch, ll, clock: Clock) -> dict:
+    """Contiguous 1 GiB write, read and copy by the hand-written stream
+    probe, best over a few grid sizes and both load/store hints: the part's
+    practical HBM rates for this kind of access."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
+    ll.ll_moe_diag_stream(ll.PROBE_WRITE, False, a, None, CEILING_BYTES, 4096)
+    torch.cuda.synchronize()
+    res = {}
+    for mode, name, moved in ((ll.PROBE_WRITE, "write", 1), (ll.PROBE_READ, "read", 1),
+                              (ll.PROBE_COPY, "copy", 2)):
+        best = None
+        for nt in (False, True):
+            for blocks in (1024, 4096, 16384):
+                us = clock.per_call(f"ceiling {name} nt={int(nt)} blocks={blocks}",
+                                    lambda s: ll.ll_moe_diag_stream(mode, nt, b, a, CEILING_BYTES,
+                                                                    blocks), 5)
+                gbs = moved * CEILING_BYTES / (us * 1e-6) / 1e9
+                if best is None or gbs > best["gbs"]:
+                    best = {"gbs": round(gbs, 1), "us": round(us, 2), "non_temporal": nt,
+                            "blocks": blocks}
+        res[name] = best
+    res["bytes"] = CEILING_BYTES
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure(name: str, args, torch, ll, W) -> dict:
+    """Every figure of one workload; frees its device memory before
+    returning."""
+    w = W.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    md = ll.ll_moe_layout_offsets(w.capacity, w.hidden, w.num_experts, w.dtype, 0)["msg_bytes"]
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    batches, routed, idx_host = [], [], []
+    most = np.zeros(w.num_experts, np.int64)
+    for b in range(args.batches):
+        wb = w.with_(seed=w.seed + b)
+        idx = W.routing(wb)
+        batches.append((dev_t(W.tokens(wb)), dev_t(idx), dev_t(W.weights(wb))))
+        idx_host.append(idx)
+        valid = (idx >= 0) & (idx < w.num_experts)
+        routed.append(int(valid.sum()))
+        most = np.maximum(most, np.bincount(idx[valid].ravel(), minlength=w.num_experts))
+    # distinct experts per token: every pick is routed
+    assert all(r == w.num_tokens * w.topk for r in routed)
+    # expert outputs on the rows some batch fills, the NaN poison elsewhere
+    filled = np.zeros(w.num_experts * w.capacity, bool)
+    for e in range(w.num_experts):
+        filled[e * w.capacity:e * w.capacity + min(int(most[e]), w.capacity)] = True
+    y = dev_t(W.expert_outputs(w, filled))
+    out = torch.empty((w.num_tokens, w.hidden), dtype=torch.float32, device=dev)
+    total = ll.ll_moe_layout_bytes(w.capacity, w.hidden, w.num_experts, w.dtype)
+    lay = torch.empty(total, dtype=torch.uint8, device=dev)
+    for q in (0, 1):
+        ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q)
+
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def dispatch(s):
+        x, idx, _ = batches[s % len(batches)]
+        ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts, w.topk,
+                           w.dtype, s & 1, x, idx, sptr)
+
+    def combine(s):
+        _, idx, wt = batches[s % len(batches)]
+        ll.ll_moe_combine(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts, w.topk,
+                          w.dtype, s & 1, y, idx, wt, out, sptr)
+
+    def step(s):
+        dispatch(s)
+        combine(s)
+
+    def reset_sets():
+        # every timed region starts from clean signal words (a dispatch of
+        # set q needs set q's words at zero) and runs parity 0, 1, ...
+        for q in (0, 1):
+            ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, sptr)
+
+    clock = Clock(torch, stream, reset_sets)
+    say = lambda msg: print(f"[bench {name}] {msg}", file=sys.stderr, flush=True)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # K back-to-back steps, nothing else between them
+    step_us = clock.per_call("dispatch + combine steps", step, args.steps)
+    say(f"{args.steps} steps: {step_us:.2f} us/step")
+
+    # per-kernel launch times: K launches of one kernel back to back (parity
+    # alternating, as in the step), timed on the stream they run on
+    d_us = clock.per_call("dispatch back to back (roofline timing)", dispatch, args.steps)
+    c_us = clock.per_call("combine back to back (roofline timing)", combine, args.steps)
+    say(f"dispatch {d_us:.2f} us/launch, combine {c_us:.2f} us/launch")
+
+    # the same steps captured once as a HIP graph and replayed back to back
+    # (an even number of them, so that every replay starts on a clean set 0)
+    graph_us = None
+    if not args.no_graph:
+        gsteps = args.steps + (args.steps & 1)
+        reset_sets()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                gs = torch.cuda.current_stream().cuda_stream
+                for s in range(gsteps):
+                    x, idx, wt = batches[s % len(batches)]
+                    ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                       w.topk, w.dtype, s & 1, x, idx, gs)
+                    ll.ll_moe_combine(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                      w.topk, w.dtype, s & 1, y, idx, wt, out, gs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / gsteps
+            best = us if best is None else min(best, us)
+        graph_us = best
+        del g
+        say(f"graph replay: {graph_us:.2f} us/step")
+
+    # repeated trials of the same K steps: spread of the step time
+    trials = [clock.per_call("dispatch + combine steps (trial)", step, args.steps)
+              for _ in range(args.trials)]
+
+    # the two-phase combine on the same batches: a step is dispatch(q),
+    # combine_send(q), combine_recv(q); then each side alone, K launches
+    # back to back on one set (the expert side re-stages the same rows, its
+    # flags counting past the counts; the token side re-folds raised flags)
+    two_phase = None
+    if not args.no_two_phase:
+        # one caller-zeroed status word per token-side call
+        nwords = max(args.steps, args.warmup) + 1
+        tp_status = torch.zeros(nwords, dtype=torch.int32, device=dev)
+        spins = 1 << 20
+
+        def send(s):
+            ll.ll_moe_combine_send(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1, y,
+                                   sptr)
+
+        def recv(s, word):
+            _, idx, wt = batches[s % len(batches)]
+            ll.ll_moe_combine_recv(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
+                                   w.topk, w.dtype, s & 1, idx, wt, out, spins,
+                                   tp_status[word:word + 1], sptr)
+
+        def tp_step(s, word=None):
+            dispatch(s)
+            send(s)
+            recv(s, s if word is None else word)
+
+        def prepared_set0():
+            tp_status.zero_()
+            tp_step(0, nwords - 1)  # set 0: one step's counts and flags
+
+        def all_ready(n):
+            torch.cuda.synchronize()
+            return bool((tp_status[:n] == ll.RECV_READY).all().item())
+
+        reset_sets()
+        tp_status.zero_()
+        for s in range(args.warmup):
+            tp_step(s)
+        tp_ok = all_ready(args.warmup)
+        tp_us = clock.per_call("two-phase steps (dispatch, combine_send, combine_recv)", tp_step,
+                               args.steps, prepare=tp_status.zero_)
+        tp_ok = tp_ok and all_ready(args.steps)
+        send_us = clock.per_call("combine_send back to back on one set (after one step "
+                                 "preparing set 0)", lambda s: send(0), args.steps,
+                                 prepare=prepared_set0)
+        recv_us = clock.per_call("combine_recv back to back on one set (after one step "
+                                 "preparing set 0)", lambda s: recv(0, s), args.steps,
+                                 prepare=prepared_set0)
+        tp_ok = tp_ok and all_ready(args.steps)
+        reset_sets()
+        torch.cuda.synchronize()
+        tb = two_phase_bytes(w, md, routed[0])
+        two_phase = {
+            "us_per_step": round(tp_us, 3),
+            "fused_us_per_step": round(step_us, 3),
+            "send_us": round(send_us, 3), "recv_us": round(recv_us, 3),
+            "send_gbs": round(tb["send"] / (send_us * 1e-6) / 1e9, 2),
+            "recv_gbs": round(tb["recv"] / (recv_us * 1e-6) / 1e9, 2),
+            "bytes_per_launch": tb, "refusals": not tp_ok,
+            "traffic": {"send": stored_traffic(w.name, "send"),
+                        "recv": stored_traffic(w.name, "recv")}}
+        say(f"two-phase: {tp_us:.2f} us/step (send {send_us:.2f}, recv {recv_us:.2f}); "
+            f"fused {step_us:.2f}")
+
+    # the dispatch's expert side (ll_moe_dispatch_recv): alone, K launches on
+    # one prepared set; then (unless --no-latency) the latency from the
+    # dispatch's start to the unpacked expert inputs, with the receiver
+    # queued after the dispatch on the same stream, or already waiting on a
+    # second stream (overlapped)
+    expert_side = None
+    if not args.no_expert_side:
+        rows = w.num_experts * w.capacity
+        pb = 2 * w.hidden if w.dtype == W.BF16 else w.hidden
+        u_payload = torch.empty((rows, pb), dtype=torch.uint8, device=dev)
+        u_scales = (torch.empty((rows, w.hidden // 128), dtype=torch.float32, device=dev)
+                    if w.dtype == W.FP8_E4M3 else None)
+        u_src = torch.empty(rows, dtype=torch.int32, device=dev)
+        u_counts = torch.empty(w.num_experts, dtype=torch.int32, device=dev)
+        # one caller-zeroed status word per call
+        u_nwords = max(args.steps, args.warmup) + 1
+        u_status = torch.zeros(u_nwords, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream()
+        u_ok = True
+
+        def unpack(s, word, st=None):
+            ll.ll_moe_dispatch_recv(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1,
+                                    routed[s % len(batches)], u_payload, u_scales, u_src,
+                                    u_counts, 1 << 20, u_status[word:word + 1],
+                                    sptr if st is None else st)
+
+        def u_ready(n):
+            torch.cuda.synchronize()
+            return bool((u_status[:n] == ll.RECV_READY).all().item())
+
+        def u_prepare():
+            u_status.zero_()
+            dispatch(0)
+
+        reset_sets()
+        u_status.zero_()
+        for s in range(args.warmup):
+            dispatch(s)
+            unpack(s, s)
+        u_ok = u_ready(args.warmup)
+        unpack_us = clock.per_call("dispatch_recv back to back on one prepared set",
+                                   lambda s: unpack(0, s), args.steps, prepare=u_prepare)
+        u_ok = u_ok and u_ready(args.steps)
+        seq_step_us = clock.per_call("dispatch + dispatch_recv steps on one stream",
+                                     lambda s: (dispatch(s), unpack(s, s)), args.steps,
+                                     prepare=u_status.zero_)
+        u_ok = u_ok and u_ready(args.steps)
+
+        def latency(overlapped: bool, trials: int = 20):
+            nonlocal u_ok
+            res = []
+            for i in range(trials):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                reset_sets()
+                u_status.zero_()
+                side.wait_stream(stream)  # after the reset and the zeroing, before the hold
+                torch.cuda._sleep(HOLD_CYCLES)
+                clock.regions.append("dispatch start to expert inputs: dispatch_recv "
+                                     + ("already waiting on a second stream"
+                                        if overlapped else "queued after the dispatch"))
+                a.record(stream)
+                dispatch(i)
+                if overlapped:
+                    unpack(i, 0, side.cuda_stream)
+                    b.record(side)
+                else:
+                    unpack(i, 0)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                u_ok = u_ok and u_ready(1)
+                res.append(a.elapsed_time(b) * 1e3)
+            return float(np.median(res))
+
+        lat = None
+        if not args.no_latency:
+            lat = {"same_stream": round(latency(False), 3), "overlapped": round(latency(True), 3)}
+        torch.cuda.synchronize()
+        ub = unpack_bytes(w, md, routed[0])
+        expert_side = {
+            "unpack_us": round(unpack_us, 3),
+            "unpack_gbs": round(ub / (unpack_us * 1e-6) / 1e9, 2),
+            "bytes_per_launch": ub,
+            "sequential_steps_us": round(seq_step_us, 3),
+            "dispatch_to_inputs_us": lat,
+            "refusals": not u_ok,
+            "traffic": stored_traffic(w.name, "unpack")}
+        say(f"expert side: unpack {unpack_us:.2f} us; dispatch start to expert inputs {lat}")
+        del u_payload, u_scales, u_src, u_counts
+
+    # cold launches: before every step a 1 GiB read pass evicts L2 and the
+    # 256 MB MALL. A read leaves only clean lines behind, so no write-back of
+    # its own overlaps the timed launches (the dirty lines of the step before
+    # are written back while it reads). Event pairs time each launch; the
+    # same event pairs without the eviction give this method's warm figure
+    # (event pairs add a little to each launch, so compare the two).
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+        ll.ll_moe_diag_stream(ll.PROBE_WRITE, False, scratch, None, COLD_EVICT_BYTES, 4096)
+        torch.cuda.synchronize()
+
+        def per_launch(evict):
+            # every step queued behind the stream hold, so the GPU runs
+            # eviction, events and launches back to back, without host gaps
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(args.cold_steps)]
+            torch.cuda.synchronize()
+            clock.hold("cold: after a 1 GiB read pass, event pairs between launches" if evict
+                       else "warm: the same event pairs between launches")
+            for s in range(args.cold_steps):
+                if evict:
+                    ll.ll_moe_diag_stream(ll.PROBE_READ, False, sink, scratch, COLD_EVICT_BYTES,
+                                          4096)
+                ev[s][0].record(stream)
+                dispatch(s)
+                ev[s][1].record(stream)
+                combine(s)
+                ev[s][2].record(stream)
+            torch.cuda.synchronize()
+            ds = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+            cs = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+            return float(np.median(ds)), float(np.median(cs))
+
+        cd, cc = per_launch(True)
+        wd, wc = per_launch(False)
+        ab0 = algorithmic_bytes(w, md, routed[0])
+        cold = {"method": f"{COLD_EVICT_BYTES >> 20} MiB read pass (clean lines only) before "
+                          "every step; median of per-launch event pairs",
+                "evict_bytes": COLD_EVICT_BYTES, "steps": args.cold_steps,
+                "us_per_step": round(cd + cc, 3), "dispatch_us": round(cd, 3),
+                "combine_us": round(cc, 3),
+                "fraction_of_hbm_peak": round(ab0["total"] / ((cd + cc) * 1e-6) / 1e9 /
+                                              HBM_PEAK_GBS, 4),
+                "warm_same_method": {"us_per_step": round(wd + wc, 3),
+                                     "dispatch_us": round(wd, 3), "combine_us": round(wc, 3)}}
+        say(f"cold (after a {COLD_EVICT_BYTES >> 20} MiB read pass): dispatch {cd:.2f} us, "
+            f"combine {cc:.2f} us; warm with the same event pairs: {wd:.2f} / {wc:.2f} us")
+        del scratch, sink
+
+    ab = algorithmic_bytes(w, md, routed[0])
+
+    # floors: the dispatch's stores alone over its exact destination rows
+    # and the combine's gather alone over its exact rows (hand-written
+    # probes built on the kernels' own store and gather code), and an empty
+    # launch, each timed like the step
+    floors = None
+    if not args.no_floors:
+        rows_q = []
+        for q in (0, 1):
+            o = ll.ll_moe_layout_offsets(w.capacity, w.hidden, w.num_experts, w.dtype, q)
+            per_tok = []
+            for b in range(len(batches)):
+                r = slot_rows(idx_host[b], w.num_experts, w.capacity)
+                offs = np.empty((w.num_tokens, w.topk + 1), np.int64)
+                offs[:, 0] = o["send"] + np.arange(w.num_tokens) * md
+                offs[:, 1:] = o["recv"] + r * md
+                per_tok.append(torch.from_numpy(offs.ravel().copy()).to(dev))
+            rows_q.append(per_tok)
+        gather_rows = [torch.from_numpy(slot_rows(i, w.num_experts, w.capacity)
+                                        .astype(np.int32)).to(dev) for i in idx_host]
+        nrows = w.num_tokens * (w.topk + 1)
+        per = max(1, min(w.topk + 1, nrows // 512))
+        line = nrows * md >= 64 << 20  # the dispatch's whole-line rule
+
+        def store_rows(s):
+            ll.ll_moe_diag_store_rows(lay, rows_q[s & 1][s % len(batches)], nrows, md, per,
+                                      line, ll.PROBE_SC1, sptr)
+
+        def gather(s):
+            _, _, wt = batches[s % len(batches)]
+            ll.ll_moe_diag_gather_rows(y, w.num_experts * w.capacity, w.hidden,
+                                       gather_rows[s % len(batches)], wt, w.num_tokens, w.topk,
+                                       out, sptr)
+
+        st_us = clock.per_call("floor: dispatch's stores alone (store_rows probe)", store_rows,
+                               args.steps)
+        ga_us = clock.per_call("floor: combine's gather alone (gather_rows probe)", gather,
+                               args.steps)
+        both_us = clock.per_call("floor: store_rows + gather_rows steps",
+                                 lambda s: (store_rows(s), gather(s)), args.steps)
+        empty_us = clock.per_call("floor: empty launches", lambda s: torch.cuda._sleep(0),
+                                  args.steps)
+        # the same stores with other cache policies (context for the
+        # write-through choice)
+        policies = {}
+        for pname, pol in (("write_back", ll.PROBE_WRITE_BACK), ("nt", ll.PROBE_NT),
+                           ("sc1_nt", ll.PROBE_SC1_NT)):
+            policies[pname] = round(clock.per_call(
+                f"floor: dispatch's stores alone, {pname} stores",
+                lambda s: ll.ll_moe_diag_store_rows(lay, rows_q[s & 1][s % len(batches)], nrows,
+                                                    md, per, line, pol, sptr), args.steps), 3)
+        floors = {
+            "store_rows_us": round(st_us, 3), "store_rows_bytes": ab["dispatch_writes"],
+            "store_rows_per_workgroup": per,
+            "gather_us": round(ga_us, 3), "gather_bytes": ab["combine"],
+            "store_then_gather_us_per_step": round(both_us, 3),
+            "empty_launch_us": round(empty_us, 3),
+            "store_rows_other_policies_us": policies,
+            "step_us_at_60pct": round(ab["total"] / (0.6 * HBM_PEAK_GBS * 1e9) * 1e6, 3)}
+        say(f"floors: stores alone {st_us:.2f} us, gather alone {ga_us:.2f} us, both as steps "
+            f"{both_us:.2f} us/step, empty launch {empty_us:.2f} us; other store policies "
+            f"{policies}")
+        del rows_q, gather_rows
+
+    dom = "dispatch" if d_us >= c_us else "combine"
+    dom_us = d_us if dom == "dispatch" else c_us
+    achieved = ab[dom] / (dom_us * 1e-6) / 1e9
+    gbs = ab["total"] / (step_us * 1e-6) / 1e9
+    res = {
+        "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden": w.hidden,
+                   "num_experts": w.num_experts, "topk": w.topk,
+                   "payload": "bf16" if w.dtype == W.BF16 else "fp8_e4m3",
+                   "max_tokens": w.capacity, "parity": "alternating",
+                   "algorithmic_bytes_per_step": ab["total"]},
+        "dtype": "bf16" if w.dtype == W.BF16 else "fp8_e4m3+bf16",
+        "us_per_step": round(step_us, 3),
+        "value": round(gbs, 2),
+        "fraction_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "kernels_us": {"dispatch": round(d_us, 3), "combine": round(c_us, 3)},
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
+        "step_trials_us": {"n": len(trials),
+                           "median": round(float(np.median(trials)), 3) if trials else None,
+                           "min": round(min(trials), 3) if trials else None},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(w.name, dom),
+                     "bytes_per_launch": ab[dom], "us_per_launch": round(dom_us, 3)},
+        "kernel_fracs": {k: round(ab[k] / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                         for k, u in (("dispatch", d_us), ("combine", c_us))},
+        "cold": cold,
+        "floors": floors,
+        "two_phase_combine": two_phase,
+        "expert_side": expert_side,
+    }
+    if args.regions:
+        res["profile_regions"] = list(clock.regions)
+    del batches, y, out, lay
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -306,7 +818,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--workload", default=None,
+                    help="time one workload only (default: worst_fill, decode and decode_fp8, "
+                         "worst_fill the headline)")
     ap.add_argument("--batches", type=int, default=4,
                     help="distinct input batches cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -315,40 +829,39 @@ def main():
     ap.add_argument("--trials", type=int, default=7,
                     help="further timed repetitions of the K steps (median and min reported)")
     ap.add_argument("--no-floors", action="store_true",
-                    help="skip the plain-kernel context timings (empty launch, fill, copy)")
+                    help="skip the hand-written floor probes (stores alone, gather alone)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the contiguous write / read / copy ceilings")
     ap.add_argument("--no-two-phase", action="store_true",
                     help="skip the two-phase combine timings")
     ap.add_argument("--no-expert-side", action="store_true",
                     help="skip the expert-side receive timings")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the dispatch-to-expert-inputs latency legs (their waiting "
+                         "receivers refuse when a profiler serializes kernels)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed after evicting L2 and MALL (0: skip)")
+    ap.add_argument("--regions", action="store_true",
+                    help="list the timed regions in the JSON line (for profile summaries)")
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSV files (no GPU)")
     ap.add_argument("--trace")
+    ap.add_argument("--trace-log")
     ap.add_argument("--fetch")
+    ap.add_argument("--fetch-log")
     ap.add_argument("--write")
+    ap.add_argument("--write-log")
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device-to-device copy of BYTES five times "
+                    help="only run the hand-written device copy of BYTES five times "
                          "(calibrates the HBM byte counters against a known size)")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         summarize_profiles(args)
-        return
-
-    if args.copy_probe:
-        import torch
-        a = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda:0").fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(f"[copy-probe] copied {args.copy_probe} bytes 5 times", file=sys.stderr)
         return
 
     if args.gpus != 1:
@@ -360,382 +873,72 @@ def main():
     import combine_ll_moe_amd as ll
     import workloads as W
 
-    w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    md = ll.ll_moe_layout_offsets(w.capacity, w.hidden, w.num_experts, w.dtype, 0)["msg_bytes"]
 
-    def dev_t(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            a = a.view(np.int16)
-        return torch.from_numpy(a).to(dev)
-
-    batches = []
-    routed = []
-    for b in range(args.batches):
-        wb = w.with_(seed=w.seed + b)
-        idx = W.routing(wb)
-        batches.append((dev_t(W.tokens(wb)), dev_t(idx), dev_t(W.weights(wb))))
-        valid = (idx >= 0) & (idx < w.num_experts)
-        routed.append(int(valid.sum()))
-    # distinct experts per token: every pick is routed
-    assert all(r == w.num_tokens * w.topk for r in routed)
-    y = dev_t(W.expert_outputs(w))
-    out = torch.empty((w.num_tokens, w.hidden), dtype=torch.float32, device=dev)
-    total = ll.ll_moe_layout_bytes(w.capacity, w.hidden, w.num_experts, w.dtype)
-    lay = torch.empty(total, dtype=torch.uint8, device=dev)
-    for q in (0, 1):
-        ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q)
-
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-
-    def dispatch(s):
-        x, idx, _ = batches[s % len(batches)]
-        ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts, w.topk,
-                           w.dtype, s & 1, x, idx, sptr)
-
-    def combine(s):
-        _, idx, wt = batches[s % len(batches)]
-        ll.ll_moe_combine(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts, w.topk,
-                          w.dtype, s & 1, y, idx, wt, out, sptr)
-
-    for s in range(args.warmup):
-        dispatch(s)
-        combine(s)
-    torch.cuda.synchronize()
-
-    # The host enqueues launches more slowly than the GPU runs them at these
-    # sizes, so a short spin kernel first holds the stream while the timed
-    # launches are queued behind it: the events then time the GPU running
-    # the steps back to back, not the host's launch rate.
-    # Every timed region starts from clean signal words (a dispatch of set q
-    # needs set q's words at zero) and runs its steps with parity 0, 1, ...
-    def reset_sets():
-        for q in (0, 1):
-            ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q, sptr)
-
-    def hold_stream(prepare=None):
-        reset_sets()
-        if prepare is not None:
-            prepare()
-        torch.cuda._sleep(HOLD_CYCLES)
-
-    # timed region: K back-to-back steps, nothing else between them
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    hold_stream()
-    t0.record(stream)
-    for s in range(args.steps):
-        dispatch(s)
-        combine(s)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
-          flush=True)
-
-    # per-kernel launch times: K launches of one kernel back to back (parity
-    # alternating, as in the step), timed on the stream they run on
-    def time_kernel(fn, prepare=None):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.copy_probe:
+        nbytes = args.copy_probe - args.copy_probe % 16
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        ll.ll_moe_diag_stream(ll.PROBE_WRITE, False, a, None, nbytes, 4096)
         torch.cuda.synchronize()
-        hold_stream(prepare)
-        a.record(stream)
-        for s in range(args.steps):
-            fn(s)
-        b.record(stream)
+        for _ in range(5):
+            ll.ll_moe_diag_stream(ll.PROBE_COPY, False, b, a, nbytes, 4096)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / args.steps
+        print(f"[copy-probe] copied {nbytes} bytes 5 times", file=sys.stderr)
+        return
 
-    d_us = time_kernel(dispatch)
-    c_us = time_kernel(combine)
-    print(f"[bench] dispatch {d_us:.2f} us/launch, combine {c_us:.2f} us/launch",
-          file=sys.stderr, flush=True)
+    names = [args.workload] if args.workload else list(DEFAULT_WORKLOADS)
+    for n in names:
+        if n not in W.WORKLOADS:
+            raise SystemExit(f"unknown workload {n}; known: {sorted(W.WORKLOADS)}")
+    headline = names[0] if args.workload else HEADLINE
 
-    # the same steps captured once as a HIP graph and replayed back to back
-    # (an even number of them, so that every replay starts on a clean set 0)
-    graph_us = None
-    if not args.no_graph:
-        gsteps = args.steps + (args.steps & 1)
-        reset_sets()
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                gs = torch.cuda.current_stream().cuda_stream
-                for s in range(gsteps):
-                    x, idx, wt = batches[s % len(batches)]
-                    ll.ll_moe_dispatch(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
-                                       w.topk, w.dtype, s & 1, x, idx, gs)
-                    ll.ll_moe_combine(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
-                                      w.topk, w.dtype, s & 1, y, idx, wt, out, gs)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        best = None
-        for _ in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / gsteps
-            best = us if best is None else min(best, us)
-        graph_us = best
-        print(f"[bench] graph replay: {graph_us:.2f} us/step", file=sys.stderr, flush=True)
+    results = {}
+    for n in names:
+        results[n] = measure(n, args, torch, ll, W)
 
-    # repeated trials of the same K steps: spread of the step time
-    trials = []
-    for _ in range(args.trials):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        hold_stream()
-        a.record(stream)
-        for s in range(args.steps):
-            dispatch(s)
-            combine(s)
-        b.record(stream)
-        torch.cuda.synchronize()
-        trials.append(a.elapsed_time(b) * 1e3 / args.steps)
+    ceil = None
+    if not args.no_ceilings:
+        reset = lambda: None
+        clock = Clock(torch, torch.cuda.current_stream(), reset)
+        ceil = ceilings(torch, ll, clock)
+        print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
 
-    # the two-phase combine on the same batches: a step is dispatch(q),
-    # combine_send(q), combine_recv(q); then each side alone, K launches
-    # back to back on one set (the expert side re-stages the same rows, its
-    # flags counting past the counts; the token side re-folds raised flags)
-    two_phase = None
-    if not args.no_two_phase:
-        # one caller-zeroed status word per token-side call
-        nwords = max(args.steps, args.warmup) + 1
-        tp_status = torch.zeros(nwords, dtype=torch.int32, device=dev)
-        spins = 1 << 20
-
-        def send(s):
-            ll.ll_moe_combine_send(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1, y,
-                                   sptr)
-
-        def recv(s, word):
-            _, idx, wt = batches[s % len(batches)]
-            ll.ll_moe_combine_recv(lay, w.capacity, w.num_tokens, w.hidden, w.num_experts,
-                                   w.topk, w.dtype, s & 1, idx, wt, out, spins,
-                                   tp_status[word:word + 1], sptr)
-
-        def tp_step(s, word=None):
-            dispatch(s)
-            send(s)
-            recv(s, s if word is None else word)
-
-        def prepared_set0():
-            tp_status.zero_()
-            tp_step(0, nwords - 1)  # set 0: one step's counts and flags
-
-        def all_ready(n):
-            torch.cuda.synchronize()
-            return bool((tp_status[:n] == ll.RECV_READY).all().item())
-
-        reset_sets()
-        tp_status.zero_()
-        for s in range(args.warmup):
-            tp_step(s)
-        tp_ok = all_ready(args.warmup)
-        tp_us = time_kernel(tp_step, prepare=tp_status.zero_)
-        tp_ok = tp_ok and all_ready(args.steps)
-        send_us = time_kernel(lambda s: send(0), prepare=prepared_set0)
-        recv_us = time_kernel(lambda s: recv(0, s), prepare=prepared_set0)
-        tp_ok = tp_ok and all_ready(args.steps)
-        for q in (0, 1):
-            ll.ll_moe_clean_signals(lay, w.capacity, w.hidden, w.num_experts, w.dtype, q)
-        torch.cuda.synchronize()
-        tb = two_phase_bytes(w, md, routed[0])
-        two_phase = {
-            "us_per_step": round(tp_us, 3),
-            "fused_us_per_step": round(ms_per_step * 1e3, 3),
-            "send_us": round(send_us, 3), "recv_us": round(recv_us, 3),
-            "send_gbs": round(tb["send"] / (send_us * 1e-6) / 1e9, 2),
-            "recv_gbs": round(tb["recv"] / (recv_us * 1e-6) / 1e9, 2),
-            "bytes_per_launch": tb, "refusals": not tp_ok,
-            "traffic": {"send": stored_traffic(w.name, "send"),
-                        "recv": stored_traffic(w.name, "recv")}}
-        print(f"[bench] two-phase: {tp_us:.2f} us/step (send {send_us:.2f}, recv {recv_us:.2f}); "
-              f"fused {ms_per_step * 1e3:.2f}", file=sys.stderr, flush=True)
-
-    # the dispatch's expert side (ll_moe_dispatch_recv): alone, K launches on
-    # one prepared set; then the latency from the dispatch's start to the
-    # unpacked expert inputs, with the receiver queued after the dispatch on
-    # the same stream, or already waiting on a second stream (overlapped)
-    expert_side = None
-    if not args.no_expert_side:
-        rows = w.num_experts * w.capacity
-        pb = 2 * w.hidden if w.dtype == W.BF16 else w.hidden
-        u_payload = torch.empty((rows, pb), dtype=torch.uint8, device=dev)
-        u_scales = (torch.empty((rows, w.hidden // 128), dtype=torch.float32, device=dev)
-                    if w.dtype == W.FP8_E4M3 else None)
-        u_src = torch.empty(rows, dtype=torch.int32, device=dev)
-        u_counts = torch.empty(w.num_experts, dtype=torch.int32, device=dev)
-        # one caller-zeroed status word per call
-        u_nwords = max(args.steps, args.warmup) + 1
-        u_status = torch.zeros(u_nwords, dtype=torch.int32, device=dev)
-        side = torch.cuda.Stream()
-        u_ok = True
-
-        def unpack(s, word, st=None):
-            ll.ll_moe_dispatch_recv(lay, w.capacity, w.hidden, w.num_experts, w.dtype, s & 1,
-                                    routed[s % len(batches)], u_payload, u_scales, u_src,
-                                    u_counts, 1 << 20, u_status[word:word + 1],
-                                    sptr if st is None else st)
-
-        def u_ready(n):
-            torch.cuda.synchronize()
-            return bool((u_status[:n] == ll.RECV_READY).all().item())
-
-        def u_prepare():
-            u_status.zero_()
-            dispatch(0)
-
-        reset_sets()
-        u_status.zero_()
-        for s in range(args.warmup):
-            dispatch(s)
-            unpack(s, s)
-        u_ok = u_ready(args.warmup)
-        unpack_us = time_kernel(lambda s: unpack(0, s), prepare=u_prepare)
-        u_ok = u_ok and u_ready(args.steps)
-        seq_step_us = time_kernel(lambda s: (dispatch(s), unpack(s, s)), prepare=u_status.zero_)
-        u_ok = u_ok and u_ready(args.steps)
-
-        def latency(overlapped: bool, trials: int = 20):
-            nonlocal u_ok
-            res = []
-            for i in range(trials):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                reset_sets()
-                u_status.zero_()
-                side.wait_stream(stream)  # after the reset and the zeroing, before the hold
-                torch.cuda._sleep(HOLD_CYCLES)
-                a.record(stream)
-                dispatch(i)
-                if overlapped:
-                    unpack(i, 0, side.cuda_stream)
-                    b.record(side)
-                else:
-                    unpack(i, 0)
-                    b.record(stream)
-                torch.cuda.synchronize()
-                u_ok = u_ok and u_ready(1)
-                res.append(a.elapsed_time(b) * 1e3)
-            return float(np.median(res))
-
-        lat_seq = latency(False)
-        lat_ovl = latency(True)
-        torch.cuda.synchronize()
-        ub = unpack_bytes(w, md, routed[0])
-        expert_side = {
-            "unpack_us": round(unpack_us, 3),
-            "unpack_gbs": round(ub / (unpack_us * 1e-6) / 1e9, 2),
-            "bytes_per_launch": ub,
-            "sequential_steps_us": round(seq_step_us, 3),
-            "dispatch_to_inputs_us": {"same_stream": round(lat_seq, 3),
-                                      "overlapped": round(lat_ovl, 3)},
-            "refusals": not u_ok,
-            "traffic": stored_traffic(w.name, "unpack")}
-        print(f"[bench] expert side: unpack {unpack_us:.2f} us; dispatch start to expert inputs "
-              f"{lat_seq:.2f} us queued after it, {lat_ovl:.2f} us overlapped",
-              file=sys.stderr, flush=True)
-
-    # cold steps: the decode working set fits in the 256 MB MALL, so back to
-    # back the step runs from cache; here a 512 MiB write evicts L2 and MALL
-    # before every step, and event pairs time each launch. The same event
-    # pairs without the eviction give the warm figure of this method (event
-    # pairs add a little to each launch, so compare the two with each other).
-    cold = None
-    if args.cold_steps > 0:
-        scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device=dev)
-
-        def per_launch(evict):
-            # every step queued behind the stream hold, so the GPU runs
-            # eviction, events and launches back to back, without host gaps
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                  for _ in range(args.cold_steps)]
-            torch.cuda.synchronize()
-            hold_stream()
-            for s in range(args.cold_steps):
-                if evict:
-                    scratch.fill_(s & 0xFF)
-                ev[s][0].record(stream)
-                dispatch(s)
-                ev[s][1].record(stream)
-                combine(s)
-                ev[s][2].record(stream)
-            torch.cuda.synchronize()
-            ds = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-            cs = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
-            return float(np.median(ds)), float(np.median(cs))
-
-        cd, cc = per_launch(True)
-        wd, wc = per_launch(False)
-        cold = {"evict_bytes": COLD_EVICT_BYTES, "steps": args.cold_steps,
-                "us_per_step": round(cd + cc, 3), "dispatch_us": round(cd, 3),
-                "combine_us": round(cc, 3),
-                "fraction_of_hbm_peak": None,
-                "warm_same_method": {"us_per_step": round(wd + wc, 3),
-                                     "dispatch_us": round(wd, 3), "combine_us": round(wc, 3)}}
-        print(f"[bench] cold (after a {COLD_EVICT_BYTES >> 20} MiB eviction): dispatch {cd:.2f} us, "
-              f"combine {cc:.2f} us; warm with the same event pairs: {wd:.2f} / {wc:.2f} us",
-              file=sys.stderr, flush=True)
-
-    ab = algorithmic_bytes(w, md, routed[0])
-    floors = None if args.no_floors else floor_probes(torch, stream, hold_stream, args.steps,
-                                                      ab["dispatch_writes"], ab["dispatch"])
-    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    if cold is not None:
-        cold["fraction_of_hbm_peak"] = round(
-            ab["total"] / (cold["us_per_step"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-    dom = "dispatch" if d_us >= c_us else "combine"
-    dom_us = d_us if dom == "dispatch" else c_us
-    achieved = ab[dom] / (dom_us * 1e-6) / 1e9
-
+    h = results[headline]
     result = {
         "metric": "dispatch+combine effective HBM GB/s (us/step alongside)",
-        "value": round(value, 2),
+        "value": h["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "us_per_step": round(ms_per_step * 1e3, 3),
+        "ms_per_step": round(h["us_per_step"] * 1e-3, 6),
+        "us_per_step": h["us_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == W.BF16 else "fp8_e4m3+bf16",
+        "dtype": h["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden": w.hidden,
-                   "num_experts": w.num_experts, "topk": w.topk,
-                   "payload": "bf16" if w.dtype == W.BF16 else "fp8_e4m3",
-                   "max_tokens": w.capacity, "parity": "alternating",
-                   "algorithmic_bytes_per_step": ab["total"]},
-        "fraction_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "kernels_us": {"dispatch": round(d_us, 3), "combine": round(c_us, 3)},
-        "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
-        "step_trials_us": {"n": len(trials),
-                           "median": round(float(np.median(trials)), 3) if trials else None,
-                           "min": round(min(trials), 3) if trials else None},
-        "cold": cold,
-        "two_phase_combine": two_phase,
-        "expert_side": expert_side,
-        "floors": floors,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(w.name, dom),
-                     "bytes_per_launch": ab[dom], "us_per_launch": round(dom_us, 3)},
+        "config": h["config"],
+        "fraction_of_hbm_peak": h["fraction_of_hbm_peak"],
+        "kernels_us": h["kernels_us"],
+        "graph_us_per_step": h["graph_us_per_step"],
+        "step_trials_us": h["step_trials_us"],
+        "cold": h["cold"],
+        "floors": h["floors"],
+        "two_phase_combine": h["two_phase_combine"],
+        "expert_side": h["expert_side"],
+        "roofline": h["roofline"],
         "cpu_baseline": None,
+        "configs": {n: {k: v for k, v in r.items() if k != "profile_regions"}
+                    for n, r in results.items()},
+        "ceilings": ceil,
     }
+    if args.regions:
+        result["profile_regions"] = h.get("profile_regions", [])
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(W.WORKLOADS[headline], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

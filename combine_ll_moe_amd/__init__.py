@@ -36,6 +36,14 @@ INTERNAL_ERROR = 3
 INVALID_ARGUMENT = 4
 INVALID_USAGE = 5
 
+PROBE_WRITE = 0
+PROBE_READ = 1
+PROBE_COPY = 2
+PROBE_SC1 = 0
+PROBE_WRITE_BACK = 1
+PROBE_NT = 2
+PROBE_SC1_NT = 3
+
 _i = ctypes.c_int
 _vp = ctypes.c_void_p
 _szp = ctypes.POINTER(ctypes.c_size_t)
@@ -51,12 +59,18 @@ _lib.ll_moe_dispatch_recv.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp
                                       _vp]
 _lib.ll_moe_clean_signals.argtypes = [_vp, _i, _i, _i, _i, _i, _vp]
 _lib.ll_moe_diag_e4m3.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+_lib.ll_moe_diag_e4m3_in_range.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 _lib.ll_moe_diag_watch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]
+_lib.ll_moe_diag_stream.argtypes = [_i, _i, _vp, _vp, ctypes.c_size_t, _i, _vp]
+_lib.ll_moe_diag_store_rows.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp]
+_lib.ll_moe_diag_gather_rows.argtypes = [_vp, ctypes.c_longlong, _i, _vp, _vp, _i, _i, _vp, _vp]
 _lib.ll_moe_status_string.argtypes = [_i]
 _lib.ll_moe_status_string.restype = ctypes.c_char_p
 for _f in ("ll_moe_layout_bytes", "ll_moe_layout_offsets", "ll_moe_dispatch",
            "ll_moe_combine", "ll_moe_combine_send", "ll_moe_combine_recv", "ll_moe_dispatch_recv",
-           "ll_moe_clean_signals", "ll_moe_diag_e4m3", "ll_moe_diag_watch"):
+           "ll_moe_clean_signals", "ll_moe_diag_e4m3", "ll_moe_diag_e4m3_in_range",
+           "ll_moe_diag_watch", "ll_moe_diag_stream",
+           "ll_moe_diag_store_rows", "ll_moe_diag_gather_rows"):
     getattr(_lib, _f).restype = _i
 
 
@@ -156,6 +170,13 @@ def ll_moe_diag_e4m3(inp, out, n: int, stream=None) -> None:
     _check(_lib.ll_moe_diag_e4m3(_ptr(inp), _ptr(out), n, _stream(stream)), "ll_moe_diag_e4m3")
 
 
+def ll_moe_diag_e4m3_in_range(inp, out, n: int, stream=None) -> None:
+    """Diagnostic: the fp8 dispatch's fast e4m3 encoder (no clamp, no NaN
+    patch), defined for |x| <= 448 * (1 + 2^-23)."""
+    _check(_lib.ll_moe_diag_e4m3_in_range(_ptr(inp), _ptr(out), n, _stream(stream)),
+           "ll_moe_diag_e4m3_in_range")
+
+
 def ll_moe_diag_watch(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
                       topk: int, parity: int, x, topk_idx, max_passes: int, report,
                       stream=None) -> None:
@@ -165,6 +186,29 @@ def ll_moe_diag_watch(layout, max_tokens: int, num_tokens: int, hidden: int, num
     _check(_lib.ll_moe_diag_watch(_ptr(layout), max_tokens, num_tokens, hidden, num_experts, topk,
                                   parity, _ptr(x), _ptr(topk_idx), max_passes, _ptr(report),
                                   _stream(stream)), "ll_moe_diag_watch")
+
+
+def ll_moe_diag_stream(mode: int, non_temporal: bool, dst, src, nbytes: int, blocks: int,
+                       stream=None) -> None:
+    """Measurement probe: a contiguous write / read / copy of nbytes."""
+    _check(_lib.ll_moe_diag_stream(mode, int(bool(non_temporal)), _ptr(dst), _ptr(src), nbytes,
+                                   blocks, _stream(stream)), "ll_moe_diag_stream")
+
+
+def ll_moe_diag_store_rows(base, row_offsets, nrows: int, row_bytes: int, rows_per_block: int,
+                           line: bool, policy: int, stream=None) -> None:
+    """Measurement probe: the dispatch's message stores alone, to listed rows."""
+    _check(_lib.ll_moe_diag_store_rows(_ptr(base), _ptr(row_offsets), nrows, row_bytes,
+                                       rows_per_block, int(bool(line)), policy, _stream(stream)),
+           "ll_moe_diag_store_rows")
+
+
+def ll_moe_diag_gather_rows(y, y_rows: int, hidden: int, rows, weights, num_tokens: int,
+                            topk: int, out, stream=None) -> None:
+    """Measurement probe: the combine's gather alone, rows handed in."""
+    _check(_lib.ll_moe_diag_gather_rows(_ptr(y), y_rows, hidden, _ptr(rows), _ptr(weights),
+                                        num_tokens, topk, _ptr(out), _stream(stream)),
+           "ll_moe_diag_gather_rows")
 
 
 def raw_status(name: str, *args) -> int:

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmoe.so")
-SOURCES = ["api.hip", "dispatch.hip", "combine.hip", "two_phase.hip", "receive.hip", "watch.hip"]
+SOURCES = ["api.hip", "dispatch.hip", "combine.hip", "two_phase.hip", "receive.hip", "watch.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

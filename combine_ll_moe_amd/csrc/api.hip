@@ -15,18 +15,15 @@ using namespace llmoe;
 
 namespace {
 
-// Launch shapes. Dispatch: a workgroup takes a tile of consecutive tokens
-// and every groups-th message of each; combine: a tile of tokens and one run
-// of columns. Tiles grow (sharing one routing prologue among more tokens)
-// once there are enough workgroups to give each of the 256 CUs about two.
-constexpr int kTargetBlocks = 512;
-constexpr int kMaxTileTokens = 2;
+// Launch shapes (the shared constants are in kernels.h). Dispatch: a
+// workgroup takes a tile of consecutive tokens and every groups-th message
+// of each; combine: a tile of tokens and one run of columns.
+//
 // The dispatch keeps one token per workgroup up to twice as many
 // workgroups: a batch of 1024 tokens of 7168 columns dispatches 7% faster
 // with 1024 one-token workgroups (four resident per CU) than with 512
 // two-token ones, whose second message waits behind the first.
 constexpr int kDispatchTileBlocks = 1024;
-constexpr uint64_t kStreamRowsBytes = 64ull << 20;
 // LDS a dispatch workgroup may use for message buffers: 64 KiB less the
 // routing prologue's share (its tile entries and its histogram).
 uint32_t dispatch_lds_budget(int num_experts) {
@@ -45,13 +42,6 @@ constexpr int64_t kWideIdxEntries = 4096;
 int wide_idx_for(const int32_t* idx, int num_tokens, int topk) {
   const int64_t entries = (int64_t)num_tokens * topk;
   return entries > kWideIdxEntries && entries % 4 == 0 && ((uintptr_t)idx & 15) == 0;
-}
-
-int tile_for(int num_tokens, int per_token_blocks, int topk, int target = kTargetBlocks) {
-  int tile = (int)(((int64_t)num_tokens * per_token_blocks) / target);
-  if (tile > kMaxTileTokens) tile = kMaxTileTokens;
-  if (tile > kMaxTileEntries / topk) tile = kMaxTileEntries / topk;
-  return tile < 1 ? 1 : tile;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -172,7 +162,7 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   p.num_experts = num_experts;
   p.topk = topk;
   p.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
-  p.tile = tile_for(num_tokens, p.slices, topk);
+  p.tile = combine_tile_for(num_tokens, p.slices, topk);
   // Large gathers stream past the caches: read with non-temporal loads they
   // leave L2 and MALL to the next dispatch's traffic (a whole step is ~20%
   // faster at 117 MB of rows); small ones gain from the cached path.
@@ -346,7 +336,14 @@ extern "C" int ll_moe_clean_signals(void* layout, int max_tokens, int hidden, in
 extern "C" int ll_moe_diag_e4m3(const float* in, uint8_t* out, size_t n, hipStream_t stream) {
   if (n == 0) return LL_MOE_SUCCESS;
   if (!in || !out || !aligned(in, 4)) return LL_MOE_INVALID_ARGUMENT;
-  return from_hip(launch_e4m3_probe(in, out, (uint64_t)n, stream));
+  return from_hip(launch_e4m3_probe(in, out, (uint64_t)n, false, stream));
+}
+
+extern "C" int ll_moe_diag_e4m3_in_range(const float* in, uint8_t* out, size_t n,
+                                         hipStream_t stream) {
+  if (n == 0) return LL_MOE_SUCCESS;
+  if (!in || !out || !aligned(in, 4)) return LL_MOE_INVALID_ARGUMENT;
+  return from_hip(launch_e4m3_probe(in, out, (uint64_t)n, true, stream));
 }
 
 extern "C" const char* ll_moe_status_string(int status) {

@@ -14,28 +14,23 @@
 // columns). It computes the tile's slots once (route.h); then, token by
 // token, every thread issues its topk 16-byte loads of bf16 expert rows at
 // once (all outstanding together), folds them with v_fma_f32 in k order,
-// and writes 8 fp32 results as two 16-byte streaming stores. Workgroup 0 zeroes the other set's
-// signal words.
+// and writes 8 fp32 results as two 16-byte streaming stores (gather.h).
+// Workgroup 0 zeroes the other set's signal words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "kernels.h"
 #include "layout.h"
 #include "route.h"
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+#include "gather.h"
 
 namespace llmoe {
 
 // Gather-reduce of token t (entry row i of the tile) over this thread's 8
-// columns. A masked pick borrows a routed pick's row address so that the
-// loads stay unconditional; its value is never used, and a token with no
-// routed pick reads nothing.
+// columns: the rows of its picks from the tile's slots, then gather_fold.
 template <int MAXK, bool STREAM>
 __device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs, int t,
                                               int i, int c, int chunks) {
-  const u32x4* y = reinterpret_cast<const u32x4*>(P.y);
   uint64_t row[MAXK];
   bool routed[MAXK];
   float w[MAXK];
@@ -48,41 +43,9 @@ __device__ __forceinline__ void combine_token(const CombineParams& P, const Rout
              (uint64_t)(routed[k] ? s : 0);
     w[k] = P.w[(uint64_t)t * P.topk + kk];
   }
-  bool any = false;
-  uint64_t fallback = 0;
-#pragma unroll
-  for (int k = MAXK - 1; k >= 0; --k) {
-    fallback = routed[k] ? row[k] : fallback;
-    any = any || routed[k];
-  }
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  if (any) {
-    u32x4 v[MAXK];
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const u32x4* src = y + (routed[k] ? row[k] : fallback) * (uint64_t)chunks + c;
-      v[k] = STREAM ? __builtin_nontemporal_load(src) : *src;
-    }
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float a = __builtin_fmaf(w[k], __uint_as_float(q[h] << 16), acc[2 * h]);
-        const float b = __builtin_fmaf(w[k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
-        acc[2 * h] = routed[k] ? a : acc[2 * h];
-        acc[2 * h + 1] = routed[k] ? b : acc[2 * h + 1];
-      }
-    }
-  }
-  // streaming (non-temporal) stores: the output is not read again here
-  f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
-  const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
-  const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
-  __builtin_nontemporal_store(lo, o);
-  __builtin_nontemporal_store(hi, o + 1);
+  gather_fold<MAXK, STREAM>(reinterpret_cast<const g32x4*>(P.y), row, routed, w, c, chunks,
+                            reinterpret_cast<gf32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) +
+                                2 * (uint64_t)c);
 }
 
 template <int MAXK, bool STREAM>

@@ -383,8 +383,11 @@ hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t strea
   return dtype == kBf16 ? launch_lines<kBf16>(p, stream) : launch_lines<kFp8>(p, stream);
 }
 
-// The fp8 encoder above, applied element-wise in groups of four; lets a test
-// compare it with an independent encoder on chosen fp32 inputs.
+// The fp8 encoders above, applied element-wise in groups of four; lets a
+// test compare them with an independent encoder on chosen fp32 inputs.
+// IN_RANGE runs the form ordinary fp8 waves use (no clamp, no NaN patch),
+// whose codes are defined for numbers of magnitude at most 448 * (1 + 2^-23).
+template <bool IN_RANGE>
 __global__ void e4m3_probe_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
                                   uint64_t n) {
   const uint64_t groups = (n + 3) / 4;
@@ -393,18 +396,23 @@ __global__ void e4m3_probe_kernel(const float* __restrict__ in, uint8_t* __restr
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = 4 * g + j < n ? in[4 * g + j] : 0.0f;
-    const uint32_t code = e4m3_code4(v[0], v[1], v[2], v[3]);
+    const uint32_t code = IN_RANGE ? e4m3_code4_in_range(v[0], v[1], v[2], v[3])
+                                   : e4m3_code4(v[0], v[1], v[2], v[3]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (4 * g + j < n) out[4 * g + j] = (uint8_t)(code >> (8 * j));
   }
 }
 
-hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, hipStream_t stream) {
+hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, bool in_range,
+                             hipStream_t stream) {
   uint64_t blocks = ((n + 3) / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks == 0) blocks = 1;
-  e4m3_probe_kernel<<<(unsigned)blocks, 256, 0, stream>>>(in, out, n);
+  if (in_range)
+    e4m3_probe_kernel<true><<<(unsigned)blocks, 256, 0, stream>>>(in, out, n);
+  else
+    e4m3_probe_kernel<false><<<(unsigned)blocks, 256, 0, stream>>>(in, out, n);
   return hipGetLastError();
 }
 

@@ -126,12 +126,34 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
 constexpr int kCombineBlock = 256;
 
+// Launch shapes shared by the combine and the gather probe. A workgroup
+// takes a tile of consecutive tokens and one run of columns; tiles grow
+// (sharing one routing prologue among more tokens) once there are enough
+// workgroups to give each of the 256 CUs about two.
+constexpr int kTargetBlocks = 512;
+constexpr int kMaxTileTokens = 2;
+constexpr int kTileEntryLimit = 64;  // tokens per tile * topk: one wavefront's lanes
+// Row gathers (and dispatches) of this many bytes or more mostly miss the
+// caches and take the streaming forms.
+constexpr uint64_t kStreamRowsBytes = 64ull << 20;
+
+inline int tile_for(int num_tokens, int per_token_blocks, int topk, int target = kTargetBlocks) {
+  int tile = (int)(((int64_t)num_tokens * per_token_blocks) / target);
+  if (tile > kMaxTileTokens) tile = kMaxTileTokens;
+  if (tile > kTileEntryLimit / topk) tile = kTileEntryLimit / topk;
+  return tile < 1 ? 1 : tile;
+}
+inline int combine_tile_for(int num_tokens, int slices, int topk) {
+  return tile_for(num_tokens, slices, topk);
+}
+
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream);
 hipError_t launch_combine_recv(const RecvParams& p, hipStream_t stream);
 hipError_t launch_dispatch_recv(const UnpackParams& p, int blocks, hipStream_t stream);
 hipError_t launch_clean(unsigned long long* sig, int num_experts, hipStream_t stream);
-hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, hipStream_t stream);
+hipError_t launch_e4m3_probe(const float* in, uint8_t* out, uint64_t n, bool in_range,
+                             hipStream_t stream);
 
 }  // namespace llmoe

@@ -24,12 +24,14 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 __device__ __forceinline__ BufRsrc message_rsrc(void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufferWord3);
 }
+template <int POLICY = kCachePolicySc1>
 __device__ __forceinline__ void store_b128(const u32x4_a4 v, BufRsrc r, uint32_t off) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kCachePolicySc1);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, POLICY);
 }
+template <int POLICY = kCachePolicySc1>
 __device__ __forceinline__ void store_b32(uint32_t v, BufRsrc r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kCachePolicySc1);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, POLICY);
 }
 
 // The first NSTAGE * blockDim 16-byte chunks of a row into registers;
@@ -59,7 +61,9 @@ __device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __rest
 // store then covers 8 whole lines instead of straddling 9; for write-through
 // stores that go to HBM this is a quarter faster. (For data the caches
 // absorb it costs a little, so the caller decides.)
-template <bool LINE>
+// POLICY is the stores' cache policy: device-coherent write-through (sc1)
+// for every message of the path; the measurement probes also time others.
+template <bool LINE, int POLICY = kCachePolicySc1>
 __device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32_t md,
                                              uint32_t part = 0, uint32_t parts = 1) {
   constexpr int kCopy = 4;
@@ -71,9 +75,9 @@ __device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32
   const uint32_t c0 = nb * part / parts;
   const uint32_t c1 = nb * (part + 1) / parts;
   if (part == 0 && tid == 0)
-    for (uint32_t b = 0; b < head; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
+    for (uint32_t b = 0; b < head; b += 4) store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
   if (part == parts - 1 && tid == 1)
-    for (uint32_t b = body_end; b < md; b += 4) store_b32(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
+    for (uint32_t b = body_end; b < md; b += 4) store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + b), rsrc, b);
   if constexpr (!LINE) {
     for (uint32_t i0 = c0 + tid; i0 < c1; i0 += kCopy * blockDim.x) {
       u32x4_a4 v[kCopy];
@@ -85,7 +89,7 @@ __device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32
 #pragma unroll
       for (int u = 0; u < kCopy; ++u) {
         const uint32_t i = i0 + u * blockDim.x;
-        if (i < c1) store_b128(v[u], rsrc, head + 16u * i);
+        if (i < c1) store_b128<POLICY>(v[u], rsrc, head + 16u * i);
       }
     }
     return;
@@ -107,7 +111,7 @@ __device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32
 #pragma unroll
     for (int u = 0; u < kCopy; ++u) {
       const uint32_t vi = v0 + u * blockDim.x;
-      if (vi >= vlo && vi < vend) store_b128(v[u], rsrc, head + 16u * (vi - sh));
+      if (vi >= vlo && vi < vend) store_b128<POLICY>(v[u], rsrc, head + 16u * (vi - sh));
     }
   }
 }

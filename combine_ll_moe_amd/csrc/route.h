@@ -31,6 +31,7 @@
 
 #include <type_traits>
 
+#include "kernels.h"
 #include "layout.h"
 
 namespace llmoe {
@@ -38,6 +39,7 @@ namespace llmoe {
 constexpr int kWave = 64;
 constexpr int kHistExperts = 4096;
 constexpr int kMaxTileEntries = kWave;  // tokens per tile * topk: one wavefront's lanes
+static_assert(kMaxTileEntries == kTileEntryLimit, "tile limits of route.h and kernels.h");
 
 // Histogram entries of the routing prologue for num_experts experts.
 __host__ __device__ constexpr int hist_cap_for(int num_experts) {

@@ -1,8 +1,9 @@
 /*
  * ll_moe_diag.h — diagnostic entry points of libllmoe.so. Not part of the
  * dispatch / combine step: one exposes a device building block so that tests
- * can compare it with an independent implementation, the other is a
- * concurrent reader of the dispatch's counts.
+ * can compare it with an independent implementation, one is a concurrent
+ * reader of the dispatch's counts, and three are measurement probes that
+ * move the step's bytes without the rest of its work.
  */
 #ifndef LL_MOE_DIAG_H_
 #define LL_MOE_DIAG_H_
@@ -28,6 +29,19 @@ extern "C" {
  * null pointer with n > 0).
  */
 int ll_moe_diag_e4m3(const float* in, uint8_t* out, size_t n, hipStream_t stream);
+
+/*
+ * ll_moe_diag_e4m3_in_range — the encoder of ll_moe_diag_e4m3 in the form
+ * the fp8 dispatch runs for every wavefront whose blocks all have a
+ * nonzero finite amax, a finite 448 / amax and no NaN: the conversion
+ * without the clamp to +-448 and without the NaN patch. In such a block
+ * every product x * (448 / amax) is a number of magnitude at most
+ * 448 * (1 + 2^-23), and for those inputs out[i] must equal
+ * ll_moe_diag_e4m3's code (values in (448, 464] round to 448). For other
+ * inputs the code is whatever the conversion gives (unspecified).
+ * Arguments and errors as for ll_moe_diag_e4m3.
+ */
+int ll_moe_diag_e4m3_in_range(const float* in, uint8_t* out, size_t n, hipStream_t stream);
 
 /*
  * ll_moe_diag_watch — a concurrent consumer of a bf16 dispatch's counts, for
@@ -60,6 +74,77 @@ int ll_moe_diag_watch(const void* layout, int max_tokens, int num_tokens, int hi
                       int num_experts, int topk, int parity, const void* x,
                       const int32_t* topk_idx, int max_passes, long long* report,
                       hipStream_t stream);
+
+/*
+ * Measurement probes. They place the step's kernels against what the part
+ * itself does with the same bytes; none of them is part of the step. The
+ * mscclpp.h comment above struct mscclppDevConn weighs a DMA engine's copy
+ * against a copy by GPU threads; on one MI355X every byte here is moved by
+ * shader loads and stores, and these probes give that path's ceilings and
+ * floors. Every call enqueues one kernel on `stream` and returns an
+ * ll_moe_status_t (INVALID_ARGUMENT for the cases named).
+ */
+#define LL_MOE_PROBE_WRITE 0  /* dst := a pattern */
+#define LL_MOE_PROBE_READ 1   /* read src (one word of dst may be written) */
+#define LL_MOE_PROBE_COPY 2   /* dst := src */
+
+/*
+ * ll_moe_diag_stream — a contiguous stream of `bytes` bytes: write, read or
+ * copy (mode above), 16-byte accesses, four in flight per thread, `blocks`
+ * workgroups of 256 threads striding over the buffer; non_temporal != 0
+ * gives the accesses the streaming (non-temporal) hint.
+ *   dst: device, 16-byte aligned, `bytes` bytes (READ: at least 16 bytes).
+ *   src: device, 16-byte aligned, `bytes` bytes (READ and COPY).
+ * INVALID_ARGUMENT: bytes % 16 != 0, blocks < 1, a null or misaligned
+ * pointer the mode needs, an unknown mode. bytes == 0 enqueues nothing.
+ */
+int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const void* src, size_t bytes,
+                       int blocks, hipStream_t stream);
+
+/* Cache policies of ll_moe_diag_store_rows' stores. */
+#define LL_MOE_PROBE_SC1 0         /* device-coherent write-through: the dispatch's */
+#define LL_MOE_PROBE_WRITE_BACK 1  /* plain stores, written back from L2 later */
+#define LL_MOE_PROBE_NT 2          /* non-temporal */
+#define LL_MOE_PROBE_SC1_NT 3      /* write-through and non-temporal */
+
+/*
+ * ll_moe_diag_store_rows — the dispatch's message stores alone: row i of
+ * the list receives row_bytes bytes of a pattern at base + row_offsets[i],
+ * from an LDS buffer, through the dispatch's store routine
+ * (destination-aligned 16-byte buffer stores of the given policy; with
+ * line != 0 the chunks are dealt to lanes by whole 128-byte lines, as the
+ * dispatch does for its largest batches). Workgroup b (256 threads) writes
+ * rows [b * rows_per_block, (b + 1) * rows_per_block). No other loads, no
+ * counts.
+ *   base:        device, 16-byte aligned.
+ *   row_offsets: device, int64 [nrows], each a multiple of 4; every row
+ *                [offset, offset + row_bytes) must lie inside base's
+ *                allocation (the caller's duty: the probe cannot see it).
+ * INVALID_ARGUMENT: nrows < 0, row_bytes not a positive multiple of 4 or
+ * above LL_MOE_MAX_MESSAGE_BYTES, rows_per_block outside [1, 256], an
+ * unknown policy, a null or misaligned pointer.
+ */
+int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows, int row_bytes,
+                           int rows_per_block, int line, int policy, hipStream_t stream);
+
+/*
+ * ll_moe_diag_gather_rows — the combine's gather alone: out[t, c] = the fma
+ * chain of ll_moe_combine over k in ascending order of
+ * fmaf(weights[t, k], y[rows[t, k], c], acc) from +0.0f, with the rows
+ * handed in instead of computed from a routing; the combine's launch shape
+ * and load forms. A row outside [0, y_rows) (a masked pick: -1) takes no
+ * part.
+ *   y:       device, bf16 [y_rows, hidden], 16-byte aligned.
+ *   rows:    device, int32 [num_tokens, topk].
+ *   weights: device, fp32 [num_tokens, topk].
+ *   out:     device, fp32 [num_tokens, hidden], 16-byte aligned.
+ * INVALID_ARGUMENT: num_tokens < 0, hidden not a positive multiple of 8,
+ * topk outside [1, LL_MOE_MAX_TOPK], y_rows < 0, a null or misaligned
+ * pointer. num_tokens == 0 enqueues nothing.
+ */
+int ll_moe_diag_gather_rows(const void* y, long long y_rows, int hidden, const int32_t* rows,
+                            const float* weights, int num_tokens, int topk, float* out,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,7 @@
 """Host-side logic of bench.py that needs no GPU: the source hash that
-decides whether the stored HBM counters still describe the kernels."""
+decides whether the stored HBM counters still describe the kernels, the row
+lists of the floor probes, and the guard that keeps counters of refused
+launches out of the profiles."""
 import os
 import shutil
 
@@ -27,7 +29,7 @@ def test_source_hash_ignores_comments_and_spacing(tmp_path):
 
 def test_source_hash_sees_code_changes(tmp_path):
     root, dst = _copy_sources(tmp_path)
-    f = dst / "api.hip"
+    f = dst / "kernels.h"
     text = f.read_text()
     assert "constexpr int kTargetBlocks = 512;" in text
     f.write_text(text.replace("constexpr int kTargetBlocks = 512;", "constexpr int kTargetBlocks = 513;"))
@@ -43,3 +45,35 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "measures one GPU" in r.stderr
+
+
+def test_floor_probe_rows_match_the_oracle_routing():
+    """The floor probes write and read exactly the rows the dispatch and the
+    combine use: the bench's stable-sort slots against the oracle's walk."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    for name in ("tiny", "decode", "wide_zipf", "worst_fill"):
+        w = W.WORKLOADS[name]
+        idx = W.routing(w)
+        slot, _ = oracle.route(idx, w.num_experts, w.capacity)
+        rows = bench.slot_rows(idx, w.num_experts, w.capacity)
+        assert np.array_equal(rows, idx.astype(np.int64) * w.capacity + slot), name
+
+
+def test_refused_counter_runs_are_not_summarized(tmp_path):
+    import json
+    import pytest
+    good = {"metric": "m", "two_phase_combine": {"refusals": False},
+            "expert_side": {"refusals": False}}
+    bad = dict(good, expert_side={"refusals": True})
+    assert bench._refusals(good) == []
+    assert bench._refusals(bad) == ["expert_side"]
+    log = tmp_path / "f.log"
+    log.write_text("[bench] noise\n" + json.dumps(bad) + "\n")
+    assert bench._bench_line(str(log)) == bad
+
+    class A:
+        fetch_log, write_log = str(log), None
+    with pytest.raises(SystemExit, match="refusals"):
+        bench.summarize_profiles(A())

@@ -388,6 +388,36 @@ def test_e4m3_encoder_against_oracle():
         assert bad.size == 0, [(hex(v.view(np.uint32)[i]), got[i], want[i]) for i in bad[:8]]
 
 
+# largest fp32 magnitude the fast encoder sees: 448 * (1 + 2^-23) rounded
+# down to a float is 448 + 2^-15, the bit pattern 0x43E00001
+FAST_DOMAIN_BITS = 0x43E00001
+
+
+def test_e4m3_fast_path_against_oracle_on_its_domain():
+    """The encoder ordinary fp8 waves run (no clamp, no NaN patch) on every
+    input of the rounding cover inside its domain, the domain's edges, and
+    16M random inputs inside it."""
+    rng = np.random.default_rng(4)
+    cover = _all_rounding_inputs()
+    mag = cover.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    cover = cover[mag <= FAST_DOMAIN_BITS]
+    edges = np.array([0x43E00001, 0x43E00000, 0x43DFFFFF, 0x43D00000, 0x43C00000, 0x43B00000,
+                      0x3B000000, 0x3A800000, 0x3A800001, 1, 0], np.uint32)
+    edges = np.concatenate([edges, edges | np.uint32(0x80000000)]).view(np.float32)
+    rnd = rng.integers(0, FAST_DOMAIN_BITS + 1, 1 << 24, dtype=np.uint64).astype(np.uint32)
+    rnd |= rng.integers(0, 2, rnd.size, dtype=np.uint32) << np.uint32(31)
+    for v in (cover, edges, rnd.view(np.float32)):
+        assert np.isfinite(v).all() and (np.abs(v) <= np.float32(448 + 2.0 ** -15)).all()
+        d_in = torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+        d_out = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+        ll.ll_moe_diag_e4m3_in_range(d_in, d_out, v.size)
+        got = d_out.cpu().numpy()
+        want = oracle.e4m3(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, [(hex(v.view(np.uint32)[i]), got[i], want[i]) for i in bad[:8]]
+    say(f"[e4m3] fast path: {cover.size} cover inputs, {edges.size} edges, {rnd.size} random")
+
+
 def test_repeated_calls_same_bits():
     """Fixed operand order: the same inputs give the same bits every call."""
     w = W.WORKLOADS["wide_zipf"]
