@@ -9,25 +9,30 @@
 // struct mscclppDevConn).
 //
 // Design on gfx950:
-//  - One or more workgroups (groups) per token. Each builds message(t) in
-//    LDS (bf16: a 16-byte-aligned copy of the row; fp8: quantized there),
-//    computes the token's slots (route.h), then streams the message from LDS
-//    to its share of the destinations: every groups-th pick's receive row
-//    and an equal part of the send row, so that no group carries a whole
-//    extra message. The send part needs no slot and goes out while the
-//    slots are being ranked.
-//  - Message rows are 4 + 2h bytes apart, so a destination starts at any
-//    4-byte phase. Stores are aligned to the destination instead: 0-3 head
-//    dwords, then whole 16-byte chunks, then 0-3 tail dwords; the LDS side
-//    absorbs the phase (dword-granular LDS reads). Large dispatches deal the
-//    chunks to lanes by whole 128-byte cache lines (copy_message).
-//  - Messages are written with device-coherent (write-through) stores;
-//    every wave waits for its own stores, then after a workgroup barrier
-//    each wavefront adds, per distinct expert among its routed picks, the
-//    number of those picks to the expert's signal word with one
-//    device-scope atomic. This is a release without an L2 write-back per
-//    workgroup (which costs tens of microseconds over a launch). The other
-//    set's signal words are zeroed by workgroup 0.
+//  - A workgroup (256 threads) takes a tile of consecutive tokens (usually
+//    one) and a group of its destination rows; `groups` workgroups share a
+//    tile (small batches: so that a launch has ~512 workgroups), each
+//    building the tile's messages in LDS (bf16: a 16-byte-aligned copy of
+//    the row; fp8: quantized there) while the routing prologue (route.h)
+//    computes the tile's slots.
+//  - Destination rows (the send row and one receive row per routed pick)
+//    go out from LDS. With wavefront rows each row is written whole by one
+//    wavefront; with group rows (bf16 messages shared among several groups)
+//    every row of the group is written by all its threads in turn, and the
+//    send row is split among the groups. Either way a receive row belongs
+//    to one group, so that group's count follows whole messages. Message rows are
+//    4 + 2h bytes apart, so a destination starts at any 4-byte phase.
+//    Stores are aligned to the destination instead: 0-3 head dwords, then
+//    whole 16-byte chunks, then 0-3 tail dwords; the LDS side absorbs the
+//    phase (dword-granular LDS reads). Large dispatches deal the chunks to
+//    lanes by whole 128-byte cache lines (copy_row_wave).
+//  - Messages are written with device-coherent (write-through) stores.
+//    Every wavefront waits for its own stores; after a workgroup barrier
+//    wavefront 0 adds one per routed pick of the group to that expert's
+//    signal word, all picks in one device-scope atomic instruction: a
+//    release without an L2 write-back (which costs tens of microseconds
+//    over a launch). The other set's signal words are zeroed by
+//    workgroup 0.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -257,19 +262,19 @@ __device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* 
   }
 }
 
-template <int DT, bool LINE, int VEC>
+template <int DT, bool LINE, int VEC, bool GROUP_ROWS>
 __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const DispatchParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ RouteShared rs;
 
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
-    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
+    for (int e = tid; e < P.num_experts; e += kDispatchBlock) P.sig_other[e] = 0;
 
-  // workgroup -> (tile of tokens [t0, t1), message group g). Workgroups
-  // are dealt to the 8 XCDs round-robin by index; all groups of one tile go
-  // to the same XCD, so the tile's rows of x come from HBM once and the
-  // other groups read them from that XCD's L2.
+  // workgroup -> (tile of tokens [t0, t1), row group g). Workgroups are
+  // dealt to the 8 XCDs round-robin by index; all groups of one tile go to
+  // the same XCD, so the tile's rows of x come from HBM once and the other
+  // groups read them from that XCD's L2.
   const int xcd = blockIdx.x % kXcds;
   const int pos = blockIdx.x / kXcds;
   const int tile = xcd + kXcds * (pos / P.groups);
@@ -278,109 +283,133 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   if (t0 >= P.num_tokens) return;
   const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
   const int K = P.topk;
+  const int G = P.groups;
   const int chunks = P.hidden / 8;
   const uint32_t md = P.msg_bytes;
   const u32x4* x = reinterpret_cast<const u32x4*>(P.x);
-  auto message_buffer = [&](int i) {
-    return lds_raw + (P.nbuf == 2 ? (i & 1) : 0) * P.msg_stride + kMsgLdsOffset;
+  auto message_buffer = [&](int i) { return lds_raw + i * P.msg_stride + kMsgLdsOffset; };
+  const int wave = tid / kWave;
+  constexpr int kWaves = kDispatchBlock / kWave;
+
+  // Destination rows of the tile: row rho = i * (K + 1) + m of token t0 + i
+  // is its send row (m = 0) or the receive row of pick m - 1. Rows by
+  // wavefront (GROUP_ROWS false): group g takes the rows rho = g,
+  // g + groups, ..., and of those wavefront w every kWaves-th from the
+  // w-th, each written whole by that wavefront. Rows by group (GROUP_ROWS):
+  // group g takes part g of groups of every send row and the whole receive
+  // rows of the picks m - 1 = g, g + groups, ..., each row written by all
+  // its threads. Either way a receive row belongs to one group, so a count
+  // raised by that group follows whole messages.
+  auto owns_pick = [&](int i, int k) {
+    const int rho = GROUP_ROWS ? k : i * (K + 1) + k + 1;
+    return rho - (rho / G) * G == g;
   };
 
   // 1. the routing prologue; the loads of x[t0] go out with its first
-  //    loads, and message(t0) is built in LDS once they are back. The send
-  //    row needs no slot: this group's part of it goes out as soon as the
-  //    message is complete; then every wavefront ranks its own copy of the
-  //    tile's slots and goes on to its receive rows without waiting for
-  //    the others.
+  //    loads, and message(t0) is built in LDS once they are back, before
+  //    the prologue's last barrier. Every wavefront then holds the tile's
+  //    slots in its own lanes.
   constexpr int kStage = 4;
   u32x4 r[kStage];
   const int wslot = route_tile<VEC, true>(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
-      reinterpret_cast<int*>(lds_raw + P.nbuf * P.msg_stride), hist_cap_for(P.num_experts),
+      reinterpret_cast<int*>(lds_raw + P.tile * P.msg_stride), hist_cap_for(P.num_experts),
       [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
       [&]() {
         build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
-      },
-      [&]() { copy_message<LINE>(P.send + (uint64_t)t0 * md, message_buffer(0), md, g, P.groups); });
-
-  // 2. per token: build message(t) (double-buffered, so one barrier), fetch
-  //    x[t + 1] while the stores of t go out, and write message(t) to the
-  //    destinations of this group: part g of the send row, and receive rows
-  //    of the picks m = g, g + groups, ... (a masked pick has none)
-  for (int t = t0; t < t1; ++t) {
-    const int i = t - t0;
-    uint8_t* msg = message_buffer(i);
-    if (i > 0) {
-      if (P.nbuf == 1) __syncthreads();  // the single buffer is still being read
-      build_message<DT, kStage>(msg, t, x + (size_t)t * chunks, P.hidden, r);
-      __syncthreads();
-      copy_message<LINE>(P.send + (uint64_t)t * md, msg, md, g, P.groups);
+      });
+  if (t1 - t0 > 1) {  // uniform: the tile's further messages, then one barrier
+    for (int t = t0 + 1; t < t1; ++t) {
+      load_row<kStage>(r, x + (size_t)t * chunks, chunks);
+      build_message<DT, kStage>(message_buffer(t - t0), t, x + (size_t)t * chunks, P.hidden, r);
     }
-    if (t + 1 < t1) load_row<kStage>(r, x + (size_t)(t + 1) * chunks, chunks);
-    for (int m = g; m < K; m += P.groups) {
-      // this wavefront's own copy of the slot; the expert was in LDS before
-      // the prologue's last barrier
-      const int s = __builtin_amdgcn_readlane(wslot, i * K + m);
-      if (s < 0) continue;
-      copy_message<LINE>(
-          P.recv + ((uint64_t)rs.expert[i * K + m] * (uint64_t)P.max_tokens + (uint64_t)s) * md, msg, md);
+    __syncthreads();
+  }
+
+  // 2. the rows
+  if constexpr (GROUP_ROWS) {
+    for (int i = 0; i < t1 - t0; ++i) {
+      const uint8_t* msg = message_buffer(i);
+      copy_message<LINE>(P.send + (uint64_t)(t0 + i) * md, msg, md, g, G);
+      for (int k = g; k < K; k += G) {
+        const int j = i * K + k;
+        const int s = __builtin_amdgcn_readlane(wslot, j);
+        if (s < 0) continue;  // masked
+        copy_message<LINE>(
+            P.recv + ((uint64_t)rs.expert[j] * (uint64_t)P.max_tokens + (uint64_t)s) * md, msg, md);
+      }
+    }
+  } else {
+    const int rows = (t1 - t0) * (K + 1);
+    for (int rho = g + G * wave; rho < rows; rho += G * kWaves) {  // uniform per wavefront
+      const int i = rho / (K + 1);
+      const int m = rho - i * (K + 1);
+      if (m == 0) {
+        copy_row_wave<LINE>(P.send + (uint64_t)(t0 + i) * md, message_buffer(i), md);
+      } else {
+        const int j = i * K + m - 1;
+        const int s = __builtin_amdgcn_readlane(wslot, j);
+        if (s < 0) continue;  // masked
+        copy_row_wave<LINE>(
+            P.recv + ((uint64_t)rs.expert[j] * (uint64_t)P.max_tokens + (uint64_t)s) * md,
+            message_buffer(i), md);
+      }
     }
   }
 
-  // 3. every wave waits until its own device-coherent stores are complete;
-  //    after the barrier, all of this workgroup's messages are visible at
-  //    device scope
+  // 3. publish: every wave waits until its own device-coherent stores are
+  //    complete; after the barrier all of this group's messages are visible
+  //    at device scope, and wavefront 0 adds one per routed pick of the
+  //    group to that expert's signal word, all in one device-scope atomic
+  //    instruction (lane j: entry j of the tile). The messages were written
+  //    with device-coherent stores that have all completed, so the adds
+  //    need no cache write-back of their own: a reader that loads the count
+  //    with acquire semantics at device scope (which invalidates its L2
+  //    copy) sees the messages. One instruction for the whole group matters
+  //    when experts share a signal line: the lanes that name one line go to
+  //    memory together, where one instruction per pick puts each add on the
+  //    contended line alone (a batch of 128 tokens over 8 experts, whose
+  //    words share one line, dispatched in 4.6 us against 6.3).
+  //    The add is a 32-bit atomic on the word's low half (little-endian): a
+  //    set's words start at 0 and a dispatch adds at most num_tokens * topk
+  //    < 2^31, so no carry reaches the high half.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-
-  // 4. publish: per wavefront-chunk of the tile's entries, one device-scope
-  //    add per expert this workgroup wrote to, of its number of messages.
-  //    The messages were written with device-coherent stores that have all
-  //    completed (step 3), so the adds need no cache write-back of their
-  //    own: a reader that loads the count with acquire semantics at device
-  //    scope (which invalidates its L2 copy) sees the messages.
-  //    The add is a 32-bit atomic on the word's low half (little-endian):
-  //    a set's words start at 0 and a dispatch adds at most
-  //    num_tokens * topk < 2^31, so no carry reaches the high half, and the
-  //    memory-side atomic unit serves 32-bit adds to a contended line
-  //    faster (6% of a dispatch whose hot experts share one line).
-  const int n = (t1 - t0) * K;
-  const int wave = tid / kWave;
-  for (int j0 = wave * kWave; j0 < n; j0 += (int)(blockDim.x / kWave) * kWave) {
-    const int j = j0 + (tid & (kWave - 1));
-    int e = -1;
-    if (j < n) {
-      const int k = j - (j / K) * K;
-      if (k - (k / P.groups) * P.groups == g && rs.slot[j] >= 0) e = rs.expert[j];
-    }
-    int group = 0;  // messages to e from this chunk, on the lowest lane naming e
-    for_each_distinct(e, [&](int v, uint64_t same) {
-      if (e == v && (same & lanes_below()) == 0) group = __popcll(same);
-    });
-    if (group > 0)
-      __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + e), (unsigned int)group,
+  if (tid < (t1 - t0) * K) {  // wavefront 0: tile * topk <= 64 entries
+    const int i = tid / K;
+    if (owns_pick(i, tid - i * K) && wslot >= 0)
+      __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + rs.expert[tid]), 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <int DT, bool LINE, int VEC>
+template <int DT, bool LINE, int VEC, bool GROUP_ROWS>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   // whole rounds of kXcds tiles, so that the index mapping covers every tile
   const int rounds = (tiles + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)p.nbuf * p.msg_stride + sizeof(int) * hist_cap_for(p.num_experts);
-  dispatch_kernel<DT, LINE, VEC><<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
+  const size_t lds = (size_t)p.tile * p.msg_stride + sizeof(int) * hist_cap_for(p.num_experts);
+  dispatch_kernel<DT, LINE, VEC, GROUP_ROWS>
+      <<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool GROUP_ROWS>
 static hipError_t launch_lines(const DispatchParams& p, hipStream_t stream) {
   if (p.line_align)
-    return p.wide_idx ? launch_dt<DT, true, 4>(p, stream) : launch_dt<DT, true, 1>(p, stream);
-  return p.wide_idx ? launch_dt<DT, false, 4>(p, stream) : launch_dt<DT, false, 1>(p, stream);
+    return p.wide_idx ? launch_dt<DT, true, 4, GROUP_ROWS>(p, stream)
+                      : launch_dt<DT, true, 1, GROUP_ROWS>(p, stream);
+  return p.wide_idx ? launch_dt<DT, false, 4, GROUP_ROWS>(p, stream)
+                    : launch_dt<DT, false, 1, GROUP_ROWS>(p, stream);
+}
+
+template <int DT>
+static hipError_t launch_modes(const DispatchParams& p, hipStream_t stream) {
+  return p.group_rows ? launch_lines<DT, true>(p, stream) : launch_lines<DT, false>(p, stream);
 }
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream) {
-  return dtype == kBf16 ? launch_lines<kBf16>(p, stream) : launch_lines<kFp8>(p, stream);
+  return dtype == kBf16 ? launch_modes<kBf16>(p, stream) : launch_modes<kFp8>(p, stream);
 }
 
 // The fp8 encoders above, applied element-wise in groups of four; lets a

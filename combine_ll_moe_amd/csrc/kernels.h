@@ -20,10 +20,10 @@ struct DispatchParams {
   int num_experts;
   int topk;
   int tile;                        // consecutive tokens per workgroup
-  int groups;                      // workgroups per tile (each takes every groups-th message)
+  int groups;                      // workgroups per tile (each takes every groups-th row)
+  int group_rows;                  // rows written by whole workgroups (else by wavefronts)
   uint32_t msg_bytes;              // md
-  uint32_t msg_stride;             // bytes of one LDS message buffer
-  int nbuf;                        // LDS message buffers (2: double-buffered)
+  uint32_t msg_stride;             // bytes of one LDS message buffer (one per tile token)
   int line_align;                  // deal store chunks to lanes by whole cache lines
   int wide_idx;                    // routing prologue reads 4 entries per load
 };
