@@ -336,7 +336,7 @@ def ceilings(torch, ll, clock: Clock) -> dict:
                               (ll.PROBE_COPY, "copy", 2)):
         best = None
         for nt in (False, True):
-            for blocks in (1024, 4096, 16384):
+            for blocks in (4096, 16384, 65536):
                 us = clock.per_call(f"ceiling {name} nt={int(nt)} blocks={blocks}",
                                     lambda s: ll.ll_moe_diag_stream(mode, nt, b, a, CEILING_BYTES,
                                                                     blocks), 5)
@@ -497,7 +497,7 @@ def measure(name: str, args, torch, ll, W) -> dict:
 
         def all_ready(n):
             torch.cuda.synchronize()
-            return bool((tp_status[:n] == ll.RECV_READY).all().item())
+            return bool(((tp_status[:n] & ~ll.RECV_WAITED) == ll.RECV_READY).all().item())
 
         reset_sets()
         tp_status.zero_()
@@ -557,7 +557,7 @@ def measure(name: str, args, torch, ll, W) -> dict:
 
         def u_ready(n):
             torch.cuda.synchronize()
-            return bool((u_status[:n] == ll.RECV_READY).all().item())
+            return bool(((u_status[:n] & ~ll.RECV_WAITED) == ll.RECV_READY).all().item())
 
         def u_prepare():
             u_status.zero_()
@@ -576,6 +576,8 @@ def measure(name: str, args, torch, ll, W) -> dict:
                                      lambda s: (dispatch(s), unpack(s, s)), args.steps,
                                      prepare=u_status.zero_)
         u_ok = u_ok and u_ready(args.steps)
+
+        waited = {"same_stream": 0, "overlapped": 0}
 
         def latency(overlapped: bool, trials: int = 20):
             nonlocal u_ok
@@ -600,12 +602,15 @@ def measure(name: str, args, torch, ll, W) -> dict:
                     b.record(stream)
                 torch.cuda.synchronize()
                 u_ok = u_ok and u_ready(1)
+                if int(u_status[0].item()) & ll.RECV_WAITED:
+                    waited["overlapped" if overlapped else "same_stream"] += 1
                 res.append(a.elapsed_time(b) * 1e3)
             return float(np.median(res))
 
         lat = None
         if not args.no_latency:
-            lat = {"same_stream": round(latency(False), 3), "overlapped": round(latency(True), 3)}
+            lat = {"same_stream": round(latency(False), 3), "overlapped": round(latency(True), 3),
+                   "trials": 20, "receiver_waited": waited}
         torch.cuda.synchronize()
         ub = unpack_bytes(w, md, routed[0])
         expert_side = {
@@ -695,9 +700,9 @@ def measure(name: str, args, torch, ll, W) -> dict:
         per = max(1, min(w.topk + 1, nrows // 512))
         line = nrows * md >= 64 << 20  # the dispatch's whole-line rule
 
-        def store_rows(s):
+        def store_rows(s, wave_rows, policy=ll.PROBE_SC1):
             ll.ll_moe_diag_store_rows(lay, rows_q[s & 1][s % len(batches)], nrows, md, per,
-                                      line, ll.PROBE_SC1, sptr)
+                                      line, wave_rows, policy, sptr)
 
         def gather(s):
             _, _, wt = batches[s % len(batches)]
@@ -705,12 +710,17 @@ def measure(name: str, args, torch, ll, W) -> dict:
                                        gather_rows[s % len(batches)], wt, w.num_tokens, w.topk,
                                        out, sptr)
 
-        st_us = clock.per_call("floor: dispatch's stores alone (store_rows probe)", store_rows,
-                               args.steps)
+        # the dispatch's two store routines: rows by workgroup, rows by wavefront
+        st_group = clock.per_call("floor: dispatch's stores alone, rows by workgroup "
+                                  "(store_rows probe)", lambda s: store_rows(s, False), args.steps)
+        st_wave = clock.per_call("floor: dispatch's stores alone, rows by wavefront "
+                                 "(store_rows probe)", lambda s: store_rows(s, True), args.steps)
+        best_wave = st_wave <= st_group
+        st_us = min(st_group, st_wave)
         ga_us = clock.per_call("floor: combine's gather alone (gather_rows probe)", gather,
                                args.steps)
         both_us = clock.per_call("floor: store_rows + gather_rows steps",
-                                 lambda s: (store_rows(s), gather(s)), args.steps)
+                                 lambda s: (store_rows(s, best_wave), gather(s)), args.steps)
         empty_us = clock.per_call("floor: empty launches", lambda s: torch.cuda._sleep(0),
                                   args.steps)
         # the same stores with other cache policies (context for the
@@ -720,17 +730,19 @@ def measure(name: str, args, torch, ll, W) -> dict:
                            ("sc1_nt", ll.PROBE_SC1_NT)):
             policies[pname] = round(clock.per_call(
                 f"floor: dispatch's stores alone, {pname} stores",
-                lambda s: ll.ll_moe_diag_store_rows(lay, rows_q[s & 1][s % len(batches)], nrows,
-                                                    md, per, line, pol, sptr), args.steps), 3)
+                lambda s: store_rows(s, best_wave, pol), args.steps), 3)
         floors = {
             "store_rows_us": round(st_us, 3), "store_rows_bytes": ab["dispatch_writes"],
+            "store_rows_by_workgroup_us": round(st_group, 3),
+            "store_rows_by_wavefront_us": round(st_wave, 3),
             "store_rows_per_workgroup": per,
             "gather_us": round(ga_us, 3), "gather_bytes": ab["combine"],
             "store_then_gather_us_per_step": round(both_us, 3),
             "empty_launch_us": round(empty_us, 3),
             "store_rows_other_policies_us": policies,
             "step_us_at_60pct": round(ab["total"] / (0.6 * HBM_PEAK_GBS * 1e9) * 1e6, 3)}
-        say(f"floors: stores alone {st_us:.2f} us, gather alone {ga_us:.2f} us, both as steps "
+        say(f"floors: stores alone {st_group:.2f} (rows by workgroup) / {st_wave:.2f} "
+            f"(by wavefront) us, gather alone {ga_us:.2f} us, both as steps "
             f"{both_us:.2f} us/step, empty launch {empty_us:.2f} us; other store policies "
             f"{policies}")
         del rows_q, gather_rows

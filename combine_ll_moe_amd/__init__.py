@@ -29,6 +29,7 @@ SEND_MAX_EXPERTS = 4096
 REFUSAL_FLAG_WAIT = 1
 REFUSAL_COUNT_WAIT = 2
 RECV_READY = 0x100
+RECV_WAITED = 0x200
 
 SUCCESS = 0
 HIP_ERROR = 1
@@ -60,9 +61,9 @@ _lib.ll_moe_dispatch_recv.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp
 _lib.ll_moe_clean_signals.argtypes = [_vp, _i, _i, _i, _i, _i, _vp]
 _lib.ll_moe_diag_e4m3.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
 _lib.ll_moe_diag_e4m3_in_range.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
-_lib.ll_moe_diag_watch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]
+_lib.ll_moe_diag_watch.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]
 _lib.ll_moe_diag_stream.argtypes = [_i, _i, _vp, _vp, ctypes.c_size_t, _i, _vp]
-_lib.ll_moe_diag_store_rows.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp]
+_lib.ll_moe_diag_store_rows.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
 _lib.ll_moe_diag_gather_rows.argtypes = [_vp, ctypes.c_longlong, _i, _vp, _vp, _i, _i, _vp, _vp]
 _lib.ll_moe_status_string.argtypes = [_i]
 _lib.ll_moe_status_string.restype = ctypes.c_char_p
@@ -178,14 +179,15 @@ def ll_moe_diag_e4m3_in_range(inp, out, n: int, stream=None) -> None:
 
 
 def ll_moe_diag_watch(layout, max_tokens: int, num_tokens: int, hidden: int, num_experts: int,
-                      topk: int, parity: int, x, topk_idx, max_passes: int, report,
-                      stream=None) -> None:
-    """Diagnostic: a concurrent consumer of a bf16 dispatch's counts; report is a
-    zeroed int64[4] (most passes of a workgroup, passes that saw a partial
-    total, violations, last total acquired)."""
+                      topk: int, dtype: int, parity: int, messages, topk_idx, max_passes: int,
+                      report, stream=None) -> None:
+    """Diagnostic: a concurrent consumer of a dispatch's counts that compares
+    whole receive rows with the expected messages; report is a zeroed
+    int64[4] (most passes of a workgroup, passes that saw a partial total,
+    violations, last total acquired)."""
     _check(_lib.ll_moe_diag_watch(_ptr(layout), max_tokens, num_tokens, hidden, num_experts, topk,
-                                  parity, _ptr(x), _ptr(topk_idx), max_passes, _ptr(report),
-                                  _stream(stream)), "ll_moe_diag_watch")
+                                  dtype, parity, _ptr(messages), _ptr(topk_idx), max_passes,
+                                  _ptr(report), _stream(stream)), "ll_moe_diag_watch")
 
 
 def ll_moe_diag_stream(mode: int, non_temporal: bool, dst, src, nbytes: int, blocks: int,
@@ -196,11 +198,11 @@ def ll_moe_diag_stream(mode: int, non_temporal: bool, dst, src, nbytes: int, blo
 
 
 def ll_moe_diag_store_rows(base, row_offsets, nrows: int, row_bytes: int, rows_per_block: int,
-                           line: bool, policy: int, stream=None) -> None:
+                           line: bool, wave_rows: bool, policy: int, stream=None) -> None:
     """Measurement probe: the dispatch's message stores alone, to listed rows."""
     _check(_lib.ll_moe_diag_store_rows(_ptr(base), _ptr(row_offsets), nrows, row_bytes,
-                                       rows_per_block, int(bool(line)), policy, _stream(stream)),
-           "ll_moe_diag_store_rows")
+                                       rows_per_block, int(bool(line)), int(bool(wave_rows)),
+                                       policy, _stream(stream)), "ll_moe_diag_store_rows")
 
 
 def ll_moe_diag_gather_rows(y, y_rows: int, hidden: int, rows, weights, num_tokens: int,

@@ -173,8 +173,9 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   p.hidden = hidden;
   p.num_experts = num_experts;
   p.topk = topk;
-  p.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
-  p.tile = combine_tile_for(num_tokens, p.slices, topk);
+  const CombineShape shape = combine_shape(num_tokens, hidden, topk);
+  p.slices = shape.slices;
+  p.tile = shape.tile;
   // Large gathers stream past the caches: read with non-temporal loads they
   // leave L2 and MALL to the next dispatch's traffic (a whole step is ~20%
   // faster at 117 MB of rows); small ones gain from the cached path.

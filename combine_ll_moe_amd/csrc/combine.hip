@@ -27,17 +27,18 @@
 namespace llmoe {
 
 // Gather-reduce of token t (entry row i of the tile) over this thread's 8
-// columns: the rows of its picks from the tile's slots, then gather_fold.
+// columns: the rows of its picks from the tile's slots (this wavefront's
+// lanes hold them, route_tile with WAVE_SLOTS), then gather_fold.
 template <int MAXK, bool STREAM>
-__device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs, int t,
-                                              int i, int c, int chunks) {
+__device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs,
+                                              int wslot, int t, int i, int c, int chunks) {
   uint64_t row[MAXK];
   bool routed[MAXK];
   float w[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
     const int kk = k < P.topk ? k : 0;
-    const int s = rs.slot[i * P.topk + kk];
+    const int s = __builtin_amdgcn_readlane(wslot, i * P.topk + kk);
     routed[k] = k < P.topk && s >= 0;
     row[k] = (uint64_t)(routed[k] ? rs.expert[i * P.topk + kk] : 0) * (uint64_t)P.max_tokens +
              (uint64_t)(routed[k] ? s : 0);
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   extern __shared__ int hist[];  // hist_cap_for(num_experts) ints
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
-    for (int e = tid; e < P.num_experts; e += blockDim.x) P.sig_other[e] = 0;
+    for (int e = tid; e < P.num_experts; e += kCombineBlock) P.sig_other[e] = 0;
 
   // workgroup -> (tile of tokens [t0, t1), run of columns sl)
   const int tile = blockIdx.x / P.slices;
@@ -63,13 +64,15 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
   if (t0 >= P.num_tokens) return;
   const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
 
-  route_tile(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs, hist,
-             hist_cap_for(P.num_experts));
+  // every wavefront holds the tile's slots in its own lanes: no barrier
+  // after the slot computation
+  const int wslot = route_tile<1, true>(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs,
+                                        hist, hist_cap_for(P.num_experts));
 
   const int chunks = P.hidden / 8;
-  const int c = sl * blockDim.x + tid;
+  const int c = sl * kCombineBlock + tid;
   if (c >= chunks) return;
-  for (int t = t0; t < t1; ++t) combine_token<MAXK, STREAM>(P, rs, t, t - t0, c, chunks);
+  for (int t = t0; t < t1; ++t) combine_token<MAXK, STREAM>(P, rs, wslot, t, t - t0, c, chunks);
 }
 
 template <bool STREAM>

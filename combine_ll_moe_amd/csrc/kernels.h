@@ -108,8 +108,11 @@ constexpr int kRecvBlocks = 512;
 constexpr int32_t kRefusalFlagWait = 1;
 constexpr int32_t kRefusalCountWait = 2;
 // Status of ll_moe_dispatch_recv and ll_moe_combine_recv: the wait ended
-// well (the counts added up; every flag came up).
+// well (the counts added up; every flag came up); and, beside it, the wait
+// found the set incomplete at its first look (the call started before the
+// work it waits for had finished).
 constexpr int32_t kStatusReady = 0x100;
+constexpr int32_t kStatusWaited = 0x200;
 
 // LDS placement of a message: it starts at this offset of its buffer, so
 // that the payload (message byte 4) is 16-byte aligned; a buffer is
@@ -143,8 +146,19 @@ inline int tile_for(int num_tokens, int per_token_blocks, int topk, int target =
   if (tile > kTileEntryLimit / topk) tile = kTileEntryLimit / topk;
   return tile < 1 ? 1 : tile;
 }
-inline int combine_tile_for(int num_tokens, int slices, int topk) {
-  return tile_for(num_tokens, slices, topk);
+// The combine's launch shape: a workgroup of kCombineBlock threads (8
+// columns each) takes a tile of `tile` tokens and a run of 2048 columns;
+// `slices` runs cover a row. (Workgroups covering a whole row, so that a
+// tile's routing prologue ran once per tile, measured slower: 1024 tokens
+// of 7168 columns 30.3 against 29.8 us.)
+struct CombineShape {
+  int slices, tile;
+};
+inline CombineShape combine_shape(int num_tokens, int hidden, int topk) {
+  CombineShape s;
+  s.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
+  s.tile = tile_for(num_tokens, s.slices, topk);
+  return s;
 }
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream);

@@ -5,10 +5,11 @@
 //  - stream: a contiguous write, read or copy of a large buffer, 16-byte
 //    accesses, four in flight per thread: the practical HBM ceilings.
 //  - store_rows: the dispatch's stores alone. Every listed destination row
-//    receives row_bytes bytes from an LDS buffer through the dispatch's own
-//    store routine (copy_message: destination-aligned 16-byte buffer
-//    stores, optionally whole-line dealing), with no loads of x, no routing
-//    and no count publish.
+//    receives row_bytes bytes from an LDS buffer through one of the
+//    dispatch's own store routines (rows by workgroup, copy_message, or by
+//    wavefront, copy_row_wave: destination-aligned 16-byte buffer stores,
+//    optionally whole-line dealing), with no loads of x, no routing and no
+//    count publish.
 //  - gather_rows: the combine's gather alone. Each token folds the listed
 //    expert-output rows through the combine's own gather_fold, in the
 //    combine's launch shape, with no routing prologue.
@@ -30,19 +31,21 @@ constexpr int kProbeBlock = 256;
 constexpr int kStreamUnroll = 4;
 constexpr int kMaxRowsPerBlock = kProbeBlock;
 
+// Workgroup b streams tiles b, b + grid, ... of kProbeBlock * kStreamUnroll
+// 16-byte chunks (16 KiB), each tile contiguous: every wavefront store or
+// load covers 1 KiB, and a workgroup's four in flight cover 16 KiB.
 template <int MODE, bool NT>
 __global__ void __launch_bounds__(kProbeBlock)
     stream_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, uint64_t n,
                   uint32_t pattern) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  constexpr uint64_t kTile = (uint64_t)kProbeBlock * kStreamUnroll;
   uint32_t acc = 0;
-  for (uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n;
-       i0 += stride * kStreamUnroll) {
+  for (uint64_t t0 = (uint64_t)blockIdx.x * kTile; t0 < n; t0 += (uint64_t)gridDim.x * kTile) {
     if constexpr (MODE == LL_MOE_PROBE_WRITE) {
-      const u32x4 v = {pattern, pattern ^ 1u, pattern ^ 2u, (uint32_t)i0};
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
-        const uint64_t j = i0 + u * stride;
+        const uint64_t j = t0 + (uint64_t)u * kProbeBlock + threadIdx.x;
+        const u32x4 v = {pattern, pattern ^ 1u, pattern ^ 2u, (uint32_t)j};
         if (j < n) {
           if (NT)
             __builtin_nontemporal_store(v, dst + j);
@@ -54,13 +57,13 @@ __global__ void __launch_bounds__(kProbeBlock)
       u32x4 v[kStreamUnroll];
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
-        const uint64_t j = i0 + u * stride;
+        const uint64_t j = t0 + (uint64_t)u * kProbeBlock + threadIdx.x;
         const uint64_t jj = j < n ? j : n - 1;
         v[u] = NT ? __builtin_nontemporal_load(src + jj) : src[jj];
       }
 #pragma unroll
       for (int u = 0; u < kStreamUnroll; ++u) {
-        const uint64_t j = i0 + u * stride;
+        const uint64_t j = t0 + (uint64_t)u * kProbeBlock + threadIdx.x;
         if constexpr (MODE == LL_MOE_PROBE_READ) {
           acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         } else if (j < n) {
@@ -91,7 +94,7 @@ hipError_t launch_stream_mode(bool nt, u32x4* dst, const u32x4* src, uint64_t n,
 // Workgroup b writes rows [b * per, (b + 1) * per) of the list. Its LDS
 // holds the row offsets, then one message buffer at the dispatch's LDS
 // placement filled with a pattern.
-template <bool LINE, int POLICY>
+template <bool LINE, int POLICY, bool WAVE_ROWS>
 __global__ void __launch_bounds__(kProbeBlock)
     store_rows_kernel(uint8_t* base, const int64_t* __restrict__ off, int nrows,
                       uint32_t row_bytes, int per, uint32_t offs_bytes) {
@@ -105,33 +108,40 @@ __global__ void __launch_bounds__(kProbeBlock)
   for (uint32_t b = 4u * tid; b < row_bytes; b += 4u * blockDim.x)
     *reinterpret_cast<uint32_t*>(msg + b) = 0xC3C30000u ^ b;
   __syncthreads();
-  for (int r = r0; r < r1; ++r) copy_message<LINE, POLICY>(base + offs[r - r0], msg, row_bytes);
+  if constexpr (WAVE_ROWS) {
+    // the dispatch's wavefront rows: wavefront w writes rows w, w + 4, ...
+    constexpr int kWaves = kProbeBlock / 64;
+    for (int r = r0 + tid / 64; r < r1; r += kWaves)
+      copy_row_wave<LINE, POLICY>(base + offs[r - r0], msg, row_bytes);
+  } else {
+    for (int r = r0; r < r1; ++r) copy_message<LINE, POLICY>(base + offs[r - r0], msg, row_bytes);
+  }
 }
 
-template <bool LINE>
+template <bool LINE, bool WAVE_ROWS>
 hipError_t launch_store_rows_policy(int policy, uint8_t* base, const int64_t* off, int nrows,
                                     uint32_t row_bytes, int per, hipStream_t stream) {
   const uint32_t offs_bytes = ((uint32_t)per * 8u + 15u) & ~15u;
   const size_t lds = offs_bytes + ((kMsgLdsOffset + row_bytes + 15u) & ~15u);
   const int blocks = (nrows + per - 1) / per;
+#define LLMOE_STORE_ROWS(POL)                                                                 \
+  store_rows_kernel<LINE, POL, WAVE_ROWS>                                                     \
+      <<<blocks, kProbeBlock, lds, stream>>>(base, off, nrows, row_bytes, per, offs_bytes)
   switch (policy) {
     case LL_MOE_PROBE_SC1:
-      store_rows_kernel<LINE, kCachePolicySc1>
-          <<<blocks, kProbeBlock, lds, stream>>>(base, off, nrows, row_bytes, per, offs_bytes);
+      LLMOE_STORE_ROWS(kCachePolicySc1);
       break;
     case LL_MOE_PROBE_WRITE_BACK:
-      store_rows_kernel<LINE, 0>
-          <<<blocks, kProbeBlock, lds, stream>>>(base, off, nrows, row_bytes, per, offs_bytes);
+      LLMOE_STORE_ROWS(0);
       break;
     case LL_MOE_PROBE_NT:
-      store_rows_kernel<LINE, kCachePolicyNt>
-          <<<blocks, kProbeBlock, lds, stream>>>(base, off, nrows, row_bytes, per, offs_bytes);
+      LLMOE_STORE_ROWS(kCachePolicyNt);
       break;
     default:
-      store_rows_kernel<LINE, kCachePolicySc1 | kCachePolicyNt>
-          <<<blocks, kProbeBlock, lds, stream>>>(base, off, nrows, row_bytes, per, offs_bytes);
+      LLMOE_STORE_ROWS(kCachePolicySc1 | kCachePolicyNt);
       break;
   }
+#undef LLMOE_STORE_ROWS
   return hipGetLastError();
 }
 
@@ -146,7 +156,7 @@ __global__ void __launch_bounds__(kCombineBlock)
   const int tl = blockIdx.x / slices;
   const int sl = blockIdx.x - tl * slices;
   const int t0 = tl * tile;
-  const int c = sl * blockDim.x + threadIdx.x;
+  const int c = sl * kCombineBlock + threadIdx.x;
   if (t0 >= num_tokens || c >= chunks) return;
   const int t1 = t0 + tile < num_tokens ? t0 + tile : num_tokens;
   for (int t = t0; t < t1; ++t) {
@@ -214,8 +224,8 @@ extern "C" int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const v
 }
 
 extern "C" int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows,
-                                      int row_bytes, int rows_per_block, int line, int policy,
-                                      hipStream_t stream) {
+                                      int row_bytes, int rows_per_block, int line, int wave_rows,
+                                      int policy, hipStream_t stream) {
   if (nrows < 0 || row_bytes < 4 || row_bytes % 4 != 0 ||
       (uint64_t)row_bytes > kMaxMessageBytes)
     return LL_MOE_INVALID_ARGUMENT;
@@ -225,11 +235,18 @@ extern "C" int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, in
   if (!base || !row_offsets || !aligned(base, 16) || !aligned(row_offsets, 8))
     return LL_MOE_INVALID_ARGUMENT;
   uint8_t* b = static_cast<uint8_t*>(base);
-  const hipError_t e =
-      line ? launch_store_rows_policy<true>(policy, b, row_offsets, nrows, (uint32_t)row_bytes,
-                                            rows_per_block, stream)
-           : launch_store_rows_policy<false>(policy, b, row_offsets, nrows, (uint32_t)row_bytes,
-                                             rows_per_block, stream);
+  const uint32_t rb = (uint32_t)row_bytes;
+  hipError_t e;
+  if (line)
+    e = wave_rows ? launch_store_rows_policy<true, true>(policy, b, row_offsets, nrows, rb,
+                                                         rows_per_block, stream)
+                  : launch_store_rows_policy<true, false>(policy, b, row_offsets, nrows, rb,
+                                                          rows_per_block, stream);
+  else
+    e = wave_rows ? launch_store_rows_policy<false, true>(policy, b, row_offsets, nrows, rb,
+                                                          rows_per_block, stream)
+                  : launch_store_rows_policy<false, false>(policy, b, row_offsets, nrows, rb,
+                                                           rows_per_block, stream);
   return from_hip(e);
 }
 
@@ -245,17 +262,16 @@ extern "C" int ll_moe_diag_gather_rows(const void* y, long long y_rows, int hidd
     return LL_MOE_INVALID_ARGUMENT;
   if ((int64_t)num_tokens * topk > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
   const int chunks = hidden / 8;
-  const int slices = (chunks + kCombineBlock - 1) / kCombineBlock;
-  const int tile = combine_tile_for(num_tokens, slices, topk);
-  const int blocks = ((num_tokens + tile - 1) / tile) * slices;
+  const CombineShape shape = combine_shape(num_tokens, hidden, topk);
+  const int blocks = ((num_tokens + shape.tile - 1) / shape.tile) * shape.slices;
   const bool stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
   const g32x4* yy = static_cast<const g32x4*>(y);
   gf32x4* o = reinterpret_cast<gf32x4*>(out);
   if (stream_rows)
     launch_gather_rows_k<true>(blocks, yy, y_rows, rows, weights, o, num_tokens, topk, chunks,
-                               tile, slices, stream);
+                               shape.tile, shape.slices, stream);
   else
     launch_gather_rows_k<false>(blocks, yy, y_rows, rows, weights, o, num_tokens, topk, chunks,
-                                tile, slices, stream);
+                                shape.tile, shape.slices, stream);
   return from_hip(hipGetLastError());
 }

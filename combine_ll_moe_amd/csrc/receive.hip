@@ -16,7 +16,8 @@
 // the dispatch. Workgroup 0 polls the counts with relaxed device-scope
 // loads and scans them in LDS until their sum reaches the expected number,
 // at most max_spins times, and posts the outcome in a status word the
-// caller zeroed; every other workgroup looks at the counts once itself and,
+// caller zeroed (with a second bit when its first look found the set
+// incomplete, so that a caller can tell that the call did overlap); every other workgroup looks at the counts once itself and,
 // if they do not add up yet, polls that one word, then scans the (now
 // final) counts. Each takes a contiguous run of the
 // flattened (expert, slot) rows; each wavefront copies whole rows, so that a row's buffer descriptor
@@ -54,10 +55,12 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
   __shared__ int32_t posted;
   if (blockIdx.x == 0) {
     bool ready = false;
+    int32_t waited = 0;
     for (int spins = 1;; ++spins) {
       // the sum is read after the scan's barrier: one value everywhere
       if (load_count_prefix(P.sig, E, P.max_tokens, pre, wave_sum) == (uint32_t)P.expected) {
         ready = true;
+        waited = spins > 1 ? kStatusWaited : 0;
         break;
       }
       if (spins >= P.max_spins) break;
@@ -65,8 +68,8 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
       __builtin_amdgcn_s_sleep(2);
     }
     if (tid == 0)
-      __hip_atomic_fetch_or(P.status, ready ? kStatusReady : kRefusalCountWait, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.status, ready ? kStatusReady | waited : kRefusalCountWait,
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!ready) return;
   } else if (load_count_prefix(P.sig, E, P.max_tokens, pre, wave_sum) != (uint32_t)P.expected) {
     // A follower looks at the counts once itself (queued after the dispatch

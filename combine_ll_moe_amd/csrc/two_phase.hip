@@ -228,14 +228,16 @@ __global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvP
 
   // 1. bounded wait for the flags. Workgroup 0 polls every expert's flag
   //    (high half == low half; an expert that received nothing is up) and
-  //    posts the outcome in the status word; the other workgroups poll that
-  //    one word. Per-token polling by every workgroup put K flag lines per
+  //    posts the outcome in the status word (with the waited bit when its
+  //    first look found a flag down); the other workgroups poll that one
+  //    word. Per-token polling by every workgroup put K flag lines per
   //    workgroup and round onto the memory channel holding the signal words,
   //    which slowed the expert side it was waiting for (decode size: expert
   //    start to folded output 24 us overlapped against 15 us queued after).
   __shared__ int32_t posted;
   if (blockIdx.x == 0) {
     bool up = false;
+    int32_t waited = 0;
     for (int spins = 1;; ++spins) {
       bool pending = false;
       for (int e = tid; e < E; e += blockDim.x) {
@@ -244,14 +246,15 @@ __global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvP
       }
       if (!__syncthreads_or(pending)) {
         up = true;
+        waited = spins > 1 ? kStatusWaited : 0;
         break;
       }
       if (spins >= P.max_spins) break;
       __builtin_amdgcn_s_sleep(2);
     }
     if (tid == 0)
-      __hip_atomic_fetch_or(P.status, up ? kStatusReady : kRefusalFlagWait, __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(P.status, up ? kStatusReady | waited : kRefusalFlagWait,
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!up) return;
   } else {
     // A follower looks at the flags once itself (queued after the expert

@@ -191,6 +191,10 @@ int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int hidden,
 #define LL_MOE_SEND_MAX_EXPERTS 4096
 #define LL_MOE_REFUSAL_FLAG_WAIT 1
 #define LL_MOE_RECV_READY 0x100
+/* Set beside LL_MOE_RECV_READY when the waiting workgroup's first look
+ * found the set incomplete: the call started before the work it waits for
+ * had finished (it overlapped with it). Informational only. */
+#define LL_MOE_RECV_WAITED 0x200
 
 /*
  * ll_moe_combine_send — expert side: stage every received message's output
@@ -232,7 +236,9 @@ int ll_moe_combine_send(void* layout, int max_tokens, int hidden, int num_expert
  *   status:       device, int32, 4-byte aligned, zeroed by the caller. One
  *                 workgroup polls the flags and posts the outcome here for
  *                 the others: LL_MOE_RECV_READY once every expert's flag is
- *                 up (an expert that received nothing is up);
+ *                 up (an expert that received nothing is up), with
+ *                 LL_MOE_RECV_WAITED beside it when a flag was still down at
+ *                 the first look;
  *                 LL_MOE_REFUSAL_FLAG_WAIT set when a wait ran out, and out
  *                 is then unspecified. Every wait is bounded, so the launch
  *                 always ends.
@@ -286,7 +292,8 @@ int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens, int hidden
  *   status:     device, int32, 4-byte aligned, zeroed by the caller. One
  *               workgroup polls the counts and posts the outcome here for
  *               the others: LL_MOE_RECV_READY once the counts have added
- *               up; LL_MOE_REFUSAL_COUNT_WAIT set when a wait ran out (the
+ *               up (with LL_MOE_RECV_WAITED beside it when they had not at
+ *               the first look); LL_MOE_REFUSAL_COUNT_WAIT set when a wait ran out (the
  *               outputs are then unspecified). Every wait is bounded.
  * An `expected` other than the routed count is a caller error: too large,
  * the wait runs out; too small, the unpack may start early and its outputs

@@ -44,34 +44,39 @@ int ll_moe_diag_e4m3(const float* in, uint8_t* out, size_t n, hipStream_t stream
 int ll_moe_diag_e4m3_in_range(const float* in, uint8_t* out, size_t n, hipStream_t stream);
 
 /*
- * ll_moe_diag_watch — a concurrent consumer of a bf16 dispatch's counts, for
- * testing the publish order of ll_moe_dispatch: a count is raised only after
- * the messages it counts are visible at device scope (mscclpp.h, the comment
- * above struct mscclppDevConn: data first, then the signal; the receiver
- * reads data only after it has seen the signal). Enqueue it on one stream
- * while a dispatch with the same arguments runs on another. Up to 64
- * workgroups, each owning a subset of the experts, repeatedly load their
- * experts' counts of set `parity` with acquire semantics at device scope
- * and, for each expert, count the receive rows the routing will fill whose
- * header names a token routed to that expert and whose sampled payload words
- * equal that token's row of x. An expert whose acquired count exceeds the
- * rows found is a violation. A workgroup stops when its acquired counts
- * reach its experts' routed messages, or after max_passes passes.
- *   layout ... topk_idx: as for ll_moe_dispatch with dtype LL_MOE_BF16; the
- *     receive rows should hold a pattern that is no message (a header
- *     outside [0, num_tokens)) and the counts of set `parity` should be 0.
+ * ll_moe_diag_watch — a concurrent consumer of a dispatch's counts (bf16 or
+ * fp8 messages), for testing the publish order of ll_moe_dispatch: a count
+ * is raised only after the messages it counts are visible at device scope
+ * (mscclpp.h, the comment above struct mscclppDevConn: data first, then the
+ * signal; the receiver reads data only after it has seen the signal).
+ * Enqueue it on one stream while a dispatch with the same arguments runs on
+ * another. Up to 64 workgroups, each owning a subset of the experts, work
+ * out from the routing which token's message every slot of their experts
+ * will hold (slot j of expert e: the j-th entry, in (token, pick) order,
+ * naming e, below max_tokens), then repeatedly load their experts' counts
+ * of set `parity` with acquire semantics at device scope and compare, whole
+ * and byte for byte, the receive rows not yet found complete with the
+ * expected messages. An expert whose acquired count exceeds its complete
+ * rows is a violation. A workgroup stops when its acquired counts reach its
+ * experts' routed messages, or after max_passes passes.
+ *   layout, max_tokens, num_tokens, hidden, num_experts, topk, dtype,
+ *     parity, topk_idx: as for ll_moe_dispatch; the receive rows should
+ *     hold a pattern that is no message and the counts of set `parity`
+ *     should be 0.
+ *   messages: device, 4-byte aligned, [num_tokens, md] bytes: message(t)
+ *     as ll_moe_dispatch must write it (header and payload).
  *   max_passes: >= 1; bounds the run, which therefore always ends.
  *   report: device, int64[4], zero on entry; receives the largest number
  *     of passes of a workgroup, the number of passes (over all workgroups)
  *     whose acquired total was strictly between 0 and the workgroup's
  *     routed total, the number of violations, and the sum of the last
  *     acquired totals.
- * num_experts at most 2048. Returns an ll_moe_status_t (INVALID_ARGUMENT as
- * for ll_moe_dispatch, and for a larger num_experts, max_passes < 1 or a
- * null or misaligned report).
+ * num_experts at most 2048, num_tokens * topk at most 4096. Returns an
+ * ll_moe_status_t (INVALID_ARGUMENT as for ll_moe_dispatch, and for larger
+ * sizes, max_passes < 1 or a null or misaligned report or messages).
  */
 int ll_moe_diag_watch(const void* layout, int max_tokens, int num_tokens, int hidden,
-                      int num_experts, int topk, int parity, const void* x,
+                      int num_experts, int topk, int dtype, int parity, const void* messages,
                       const int32_t* topk_idx, int max_passes, long long* report,
                       hipStream_t stream);
 
@@ -110,11 +115,13 @@ int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const void* src, s
 /*
  * ll_moe_diag_store_rows — the dispatch's message stores alone: row i of
  * the list receives row_bytes bytes of a pattern at base + row_offsets[i],
- * from an LDS buffer, through the dispatch's store routine
+ * from an LDS buffer, through one of the dispatch's store routines
  * (destination-aligned 16-byte buffer stores of the given policy; with
  * line != 0 the chunks are dealt to lanes by whole 128-byte lines, as the
  * dispatch does for its largest batches). Workgroup b (256 threads) writes
- * rows [b * rows_per_block, (b + 1) * rows_per_block). No other loads, no
+ * rows [b * rows_per_block, (b + 1) * rows_per_block): with wave_rows == 0
+ * every row by all its threads in turn, with wave_rows != 0 each row whole
+ * by one wavefront (wavefront w: rows w, w + 4, ...). No other loads, no
  * counts.
  *   base:        device, 16-byte aligned.
  *   row_offsets: device, int64 [nrows], each a multiple of 4; every row
@@ -125,7 +132,8 @@ int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const void* src, s
  * unknown policy, a null or misaligned pointer.
  */
 int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows, int row_bytes,
-                           int rows_per_block, int line, int policy, hipStream_t stream);
+                           int rows_per_block, int line, int wave_rows, int policy,
+                           hipStream_t stream);
 
 /*
  * ll_moe_diag_gather_rows — the combine's gather alone: out[t, c] = the fma

@@ -108,16 +108,17 @@ def test_clean_rejects_bad_arguments():
 @pytest.mark.parametrize("case", [
     dict(parity=2), dict(num_tokens=129), dict(topk=0), dict(hidden=1020),
     dict(num_experts=2049, topk=2), dict(max_passes=0), dict(report=0), dict(report=FAKE + 4),
-    dict(layout=0), dict(x=0), dict(idx=FAKE + 1),
+    dict(layout=0), dict(msgs=0), dict(msgs=FAKE + 2), dict(idx=FAKE + 1), dict(dtype=7),
+    dict(dtype=1, hidden=1000), dict(max_tokens=4097, num_tokens=4097, topk=1),
 ])
 def test_watch_rejects_bad_arguments(case):
     import combine_ll_moe_amd as ll
     a = dict(layout=FAKE, max_tokens=128, num_tokens=128, hidden=1024, num_experts=8, topk=2,
-             parity=0, x=FAKE, idx=FAKE, max_passes=10, report=FAKE)
+             dtype=0, parity=0, msgs=FAKE, idx=FAKE, max_passes=10, report=FAKE)
     a.update(case)
     rc = ll.raw_status("ll_moe_diag_watch", a["layout"], a["max_tokens"], a["num_tokens"],
-                       a["hidden"], a["num_experts"], a["topk"], a["parity"], a["x"], a["idx"],
-                       a["max_passes"], a["report"], None)
+                       a["hidden"], a["num_experts"], a["topk"], a["dtype"], a["parity"],
+                       a["msgs"], a["idx"], a["max_passes"], a["report"], None)
     assert rc == ll.INVALID_ARGUMENT
 
 

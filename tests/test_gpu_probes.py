@@ -71,9 +71,11 @@ def test_gather_probe_skips_rows_out_of_range():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("line,policy", [(False, 0), (True, 0), (False, 1), (False, 2),
-                                         (True, 3)])
-def test_store_probe_writes_only_its_rows(line, policy):
+@pytest.mark.parametrize("line,wave_rows,policy", [(False, False, 0), (True, False, 0),
+                                                   (False, True, 0), (True, True, 0),
+                                                   (False, False, 1), (False, True, 2),
+                                                   (True, False, 3)])
+def test_store_probe_writes_only_its_rows(line, wave_rows, policy):
     row_bytes = 4 + 2 * 1000  # 4-byte phases, as message rows
     nrows, space = 37, 64
     rng = np.random.default_rng(1)
@@ -81,8 +83,8 @@ def test_store_probe_writes_only_its_rows(line, policy):
     offs = (slots * row_bytes).astype(np.int64)
     buf = torch.full((space * row_bytes + 64,), 0xA5, dtype=torch.uint8, device=DEV)
     base = buf[16:]
-    say(f"[probe] store_rows line={line} policy={policy}")
-    ll.ll_moe_diag_store_rows(base, to_dev(offs), nrows, row_bytes, 3, line, policy)
+    say(f"[probe] store_rows line={line} wave_rows={wave_rows} policy={policy}")
+    ll.ll_moe_diag_store_rows(base, to_dev(offs), nrows, row_bytes, 6, line, wave_rows, policy)
     torch.cuda.synchronize()
     got = buf.cpu().numpy()
     want = np.full_like(got, 0xA5)

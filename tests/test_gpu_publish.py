@@ -6,8 +6,10 @@ No value left behind by a finished dispatch can show this order, so a
 consumer kernel (ll_moe_diag_watch) runs on a second stream while the
 dispatch runs: it acquires the counts over and over and checks, each time,
 that every expert has at least as many complete receive rows as its
-acquired count. The receive rows start as a sentinel that is no message.
-The dispatch output is then compared with the oracle as in the parity tests.
+acquired count, a row being complete when every byte equals the message of
+the token its slot belongs to (the oracle's encoding, bf16 or fp8). The
+receive rows start as a sentinel that is no message. The dispatch output is
+then compared with the oracle as in the parity tests.
 """
 import pytest
 
@@ -34,7 +36,7 @@ MAX_PASSES = 20000
 HOLD_CYCLES = 1_200_000
 
 
-def _watched_dispatch(st: Step, q: int, x: np.ndarray, idx: np.ndarray):
+def _watched_dispatch(st: Step, q: int, x: np.ndarray, idx: np.ndarray, messages):
     w = st.w
     n, k = idx.shape
     xd, idd = to_dev(x), to_dev(idx)
@@ -48,27 +50,29 @@ def _watched_dispatch(st: Step, q: int, x: np.ndarray, idx: np.ndarray):
     torch.cuda._sleep(HOLD_CYCLES)
     ll.ll_moe_dispatch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q, xd, idd,
                        stream=main)
-    ll.ll_moe_diag_watch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, q, xd, idd,
-                         MAX_PASSES, report, stream=side)
+    ll.ll_moe_diag_watch(st.lay, w.capacity, n, w.hidden, w.num_experts, k, w.dtype, q, messages,
+                         idd, MAX_PASSES, report, stream=side)
     oracle.dispatch(st.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, x, idx)
     torch.cuda.synchronize()
     return [int(v) for v in report.cpu()]
 
 
 @pytest.mark.parametrize("name,num_tokens", [("decode", 128), ("decode", 512),
-                                             ("wide_zipf", 512)])
+                                             ("wide_zipf", 512), ("decode_fp8", 128),
+                                             ("decode_fp8", 512)])
 def test_counts_never_run_ahead_of_messages(name, num_tokens):
     w = W.WORKLOADS[name].with_(num_tokens=num_tokens)
-    assert w.dtype == W.BF16
     x, idx = W.tokens(w), W.routing(w)
     _, cnt = oracle.route(idx, w.num_experts, w.capacity)
     routed = int(cnt.sum())
+    # the messages the rows must hold, from the oracle's encoder
+    messages = to_dev(np.ascontiguousarray(oracle.encode_messages(x, w.dtype)))
     st = Step(w, full_image=False)
     partial = 0
     for rep in range(4):
         q = rep & 1
         say(f"[publish] {name} N={num_tokens} rep {rep} parity {q}")
-        passes, part, violations, last = _watched_dispatch(st, q, x, idx)
+        passes, part, violations, last = _watched_dispatch(st, q, x, idx, messages)
         say(f"[publish]   passes {passes}, partial views {part}, violations {violations}, "
             f"last total {last} of {routed}")
         assert violations == 0, "a count was visible before its messages"
@@ -78,4 +82,3 @@ def test_counts_never_run_ahead_of_messages(name, num_tokens):
     # the watcher must really have overlapped the dispatch at least once,
     # or the check above says nothing about the order
     assert partial > 0, "the watcher never saw a partial total"
-
