@@ -138,18 +138,23 @@ __device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, c
   if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = scale;
 }
 
-// Four rounds of units, u0 + s * blockDim for s = 0..3 (all threads call
-// it; units past the end are computed and not stored). A 128-element block
-// is 16 consecutive lanes, one DPP row; the row reduces amax with four DPP
-// steps (swap pairs, swap halves of quads, mirror halves of the row, mirror
-// the row). The two divisions are then made once per lane instead of once
-// per round: lane j of every quad divides for round j, and round s takes its
-// block's inv and scale from lane s of the quad (DPP quad_perm [s,s,s,s]).
-// Every lane of a row holds the same amax, so each quad has all four.
-__device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0,
-                                                const u32x4 (&raw)[4]) {
-  const int units = hidden / 8;
-  const int B = blockDim.x;
+// Block inverses and scales of four rounds of units, and whether the
+// wavefront takes the conversion without clamp and NaN patch (wave-uniform).
+struct QuantPlan {
+  float inv[4];
+  float scale[4];
+  bool fast;
+};
+
+// The plan of four rounds of units, u0 + s * blockDim for s = 0..3 (all
+// threads call it). A 128-element block is 16 consecutive lanes, one DPP
+// row; the row reduces amax with four DPP steps (swap pairs, swap halves of
+// quads, mirror halves of the row, mirror the row). The two divisions are
+// then made once per lane instead of once per round: lane j of every quad
+// divides for round j, and round s takes its block's inv and scale from
+// lane s of the quad (DPP quad_perm [s,s,s,s]). Every lane of a row holds
+// the same amax, so each quad has all four.
+__device__ __forceinline__ QuantPlan quantize_plan(const u32x4 (&raw)[4]) {
   uint32_t m[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) m[s] = max_mag_bits(raw[s]);
@@ -177,30 +182,45 @@ __device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0
     inv = 448.0f / a;
     scale = a / 448.0f;
   }
-  const float inv_s[4] = {dpp_f32<0x00>(inv), dpp_f32<0x55>(inv), dpp_f32<0xAA>(inv),
-                          dpp_f32<0xFF>(inv)};
-  const float scale_s[4] = {dpp_f32<0x00>(scale), dpp_f32<0x55>(scale), dpp_f32<0xAA>(scale),
-                            dpp_f32<0xFF>(scale)};
+  QuantPlan p;
+  p.inv[0] = dpp_f32<0x00>(inv);
+  p.inv[1] = dpp_f32<0x55>(inv);
+  p.inv[2] = dpp_f32<0xAA>(inv);
+  p.inv[3] = dpp_f32<0xFF>(inv);
+  p.scale[0] = dpp_f32<0x00>(scale);
+  p.scale[1] = dpp_f32<0x55>(scale);
+  p.scale[2] = dpp_f32<0xAA>(scale);
+  p.scale[3] = dpp_f32<0xFF>(scale);
   // A block with a finite amax, a finite inv and no NaN in this lane gives
   // products of magnitude at most 448 * (1 + 2^-23): every |x| <= amax and
   // inv is 448 / amax rounded once. Such waves skip the clamp and the NaN
   // patch; a wave with any other block keeps them.
   bool special = mm > 0x7F80u;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) special = special || amax[s] == __builtin_inff() || inv_s[s] == __builtin_inff();
-  if (__builtin_expect(__ballot(special) == 0, 1)) {
+  for (int s = 0; s < 4; ++s)
+    special = special || amax[s] == __builtin_inff() || p.inv[s] == __builtin_inff();
+  p.fast = __ballot(special) == 0;
+  return p;
+}
+
+// Round s of a plan: unit u0 + s * blockDim (if below the row's units).
+__device__ __forceinline__ void quantize_round(uint8_t* msg, int hidden, int u0, int s,
+                                               const u32x4 raw, const QuantPlan& p) {
+  const int u = u0 + s * (int)blockDim.x;
+  if (u >= hidden / 8) return;
+  if (__builtin_expect(p.fast, 1))
+    quantize_unit<true>(msg, hidden, u, raw, p.inv[s], p.scale[s]);
+  else
+    quantize_unit<false>(msg, hidden, u, raw, p.inv[s], p.scale[s]);
+}
+
+// Four rounds of units, u0 + s * blockDim for s = 0..3 (all threads call
+// it; units past the end are computed and not stored).
+__device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0,
+                                                const u32x4 (&raw)[4]) {
+  const QuantPlan p = quantize_plan(raw);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int u = u0 + s * B;
-      if (u < units) quantize_unit<true>(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int u = u0 + s * B;
-      if (u < units) quantize_unit<false>(msg, hidden, u, raw[s], inv_s[s], scale_s[s]);
-    }
-  }
+  for (int s = 0; s < 4; ++s) quantize_round(msg, hidden, u0, s, raw[s], p);
 }
 
 // fp8 message body: per 128-element block, amax over the block (NaN

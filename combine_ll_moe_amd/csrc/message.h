@@ -116,63 +116,90 @@ __device__ __forceinline__ void copy_message(void* d, const uint8_t* msg, uint32
   }
 }
 
-// One whole message from LDS to its destination, written by one wavefront
-// (all 64 lanes call it with the same arguments): 0-3 head dwords and 0-3
-// tail dwords (lanes 0-2), and the whole 16-byte body chunks between them,
-// lane-strided, eight per lane per round with the round's LDS reads issued
-// before its stores. Stores as in copy_message: destination-aligned, of the
-// given cache policy, confined to the message by the buffer descriptor;
-// LINE deals the body to lanes by whole 128-byte lines.
+// Body chunks [a, b) of one message from LDS to its destination, written by
+// one wavefront (all 64 lanes call it with the same arguments). The body
+// starts `head` bytes into the destination (head = bytes to its first
+// 16-byte boundary); chunk c is destination bytes [head + 16c, head + 16c +
+// 16). Lane-strided, eight chunks per lane per round with the round's LDS
+// reads issued before its stores; stores as in copy_message:
+// destination-aligned, of the given cache policy, confined to the message
+// by the buffer descriptor. LINE deals the chunks to lanes by whole 128-byte
+// lines (every 8 lanes of a store cover one line).
 template <bool LINE, int POLICY = kCachePolicySc1>
-__device__ __forceinline__ void copy_row_wave(void* d, const uint8_t* msg, uint32_t md) {
+__device__ __forceinline__ void copy_body_wave(void* d, const uint8_t* msg, uint32_t md,
+                                               uint32_t head, uint32_t a, uint32_t b) {
   constexpr uint32_t kCopy = 8;
   constexpr uint32_t kLanes = 64;
   const uint32_t lane = threadIdx.x & (kLanes - 1);
   const BufRsrc rsrc = message_rsrc(d, md);
-  uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
-  head = head < md ? head : md & ~3u;
-  const uint32_t nb = (md - head) >> 4;
-  const uint32_t body_end = head + 16u * nb;
-  if (4 * lane < head)
-    store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + 4 * lane), rsrc, 4 * lane);
-  if (body_end + 4 * lane < md)
-    store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + body_end + 4 * lane), rsrc,
-                      body_end + 4 * lane);
   if constexpr (!LINE) {
-    for (uint32_t i0 = lane; i0 < nb; i0 += kCopy * kLanes) {
+    for (uint32_t i0 = a + lane; i0 < b; i0 += kCopy * kLanes) {
       u32x4_a4 v[kCopy];
 #pragma unroll
       for (uint32_t u = 0; u < kCopy; ++u) {
         const uint32_t i = i0 + u * kLanes;
-        v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < nb ? i : nb - 1));
+        v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * (i < b ? i : b - 1));
       }
 #pragma unroll
       for (uint32_t u = 0; u < kCopy; ++u) {
         const uint32_t i = i0 + u * kLanes;
-        if (i < nb) store_b128<POLICY>(v[u], rsrc, head + 16u * i);
+        if (i < b) store_b128<POLICY>(v[u], rsrc, head + 16u * i);
       }
     }
   } else {
-    if (nb == 0) return;
-    // virtual indices [sh, nb + sh) hold chunks [0, nb); rounds start at
-    // multiples of 8, so every 8 lanes of a store cover one whole line
+    // virtual index vi = c + sh, sh = the body's 16-byte offset in its first
+    // line; rounds start at multiples of 8
     const uint32_t sh = (((uint32_t)(uintptr_t)d + head) & 127u) >> 4;
-    const uint32_t vend = nb + sh;
-    for (uint32_t v0 = lane; v0 < vend; v0 += kCopy * kLanes) {
+    const uint32_t vlo = a + sh, vend = b + sh;
+    for (uint32_t v0 = (vlo & ~7u) + lane; v0 < vend; v0 += kCopy * kLanes) {
       u32x4_a4 v[kCopy];
 #pragma unroll
       for (uint32_t u = 0; u < kCopy; ++u) {
         const uint32_t vi = v0 + u * kLanes;
-        const uint32_t k = vi >= sh && vi < vend ? vi - sh : 0u;
+        const uint32_t k = vi >= vlo && vi < vend ? vi - sh : a;
         v[u] = *reinterpret_cast<const u32x4_a4*>(msg + head + 16u * k);
       }
 #pragma unroll
       for (uint32_t u = 0; u < kCopy; ++u) {
         const uint32_t vi = v0 + u * kLanes;
-        if (vi >= sh && vi < vend) store_b128<POLICY>(v[u], rsrc, head + 16u * (vi - sh));
+        if (vi >= vlo && vi < vend) store_b128<POLICY>(v[u], rsrc, head + 16u * (vi - sh));
       }
     }
   }
+}
+
+// Bytes before a destination's first 16-byte boundary (at most md, whole
+// dwords).
+__device__ __forceinline__ uint32_t message_head(const void* d, uint32_t md) {
+  const uint32_t head = (16u - ((uint32_t)(uintptr_t)d & 15u)) & 15u;
+  return head < md ? head : md & ~3u;
+}
+
+// The 0-3 head dwords (bytes [0, head)) and 0-3 tail dwords (bytes
+// [head + 16 * nb, md), nb = the whole body chunks) of one message, by lanes
+// 0-2 of one wavefront.
+template <int POLICY = kCachePolicySc1>
+__device__ __forceinline__ void copy_edges_wave(void* d, const uint8_t* msg, uint32_t md,
+                                                uint32_t head) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const BufRsrc rsrc = message_rsrc(d, md);
+  const uint32_t body_end = head + 16u * ((md - head) >> 4);
+  if (4 * lane < head)
+    store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + 4 * lane), rsrc, 4 * lane);
+  if (body_end + 4 * lane < md)
+    store_b32<POLICY>(*reinterpret_cast<const uint32_t*>(msg + body_end + 4 * lane), rsrc,
+                      body_end + 4 * lane);
+}
+
+// One whole message from LDS to its destination, written by one wavefront
+// (all 64 lanes call it with the same arguments): the head and tail dwords
+// and every body chunk (copy_edges_wave, copy_body_wave).
+template <bool LINE, int POLICY = kCachePolicySc1>
+__device__ __forceinline__ void copy_row_wave(void* d, const uint8_t* msg, uint32_t md) {
+  const uint32_t head = message_head(d, md);
+  copy_edges_wave<POLICY>(d, msg, md, head);
+  const uint32_t nb = (md - head) >> 4;
+  if (nb > 0) copy_body_wave<LINE, POLICY>(d, msg, md, head, 0, nb);
 }
 
 }  // namespace llmoe

@@ -116,6 +116,16 @@ int ll_moe_layout_offsets(int max_tokens, int hidden, int num_experts, int dtype
 
 /*
  * ll_moe_dispatch — pack every token's messages into set `parity`.
+ * Defined by the rocSHMEM example "LL_MoE/LL_MoE_Buffers.hpp": struct
+ * LLMoEBuffer (the dispatch send buffer [num_tokens, hidden+1], the receive
+ * buffer [num_experts * num_tokens, hidden+1] in per-expert slots and the
+ * int64 count per expert) and the LLMoEBufferLayout constructor ("Message
+ * sizes": an int header, then hidden payload elements); the count is raised
+ * after the messages it counts as mscclpp.h's put-then-signal contract
+ * (comment above struct mscclppDevConn) orders a signal after its data. The
+ * pages do not say which slot a message takes; here slots go in ascending
+ * (token, pick) order, and the fp8 payload's quantizer (below) is likewise
+ * a reading of the pages, which give none.
  *   layout:   device, ll_moe_layout_bytes bytes, 16-byte aligned.
  *   x:        device, bf16 [num_tokens, hidden] row-major, 16-byte aligned.
  *   topk_idx: device, int32 [num_tokens, topk], 4-byte aligned.
@@ -140,6 +150,15 @@ int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int hidden,
 
 /*
  * ll_moe_combine — top-k weighted sum of the expert outputs per token.
+ * The rocSHMEM example's combine buffers (struct LLMoEBuffer: combine send
+ * and receive buffers and a flag per expert) carry the expert outputs back
+ * to their tokens; on one GPU the put and the fold collapse into one
+ * gather, as memra-engine "src/tp_ar.rs" replaces its push-then-fold
+ * all-reduce (memra_tp_ar_push, memra_tp_ar_fold) with a one-shot
+ * memra_tp_ar_1stage that reads every input in one global order, so that
+ * the result is the same bits on every call. The weighted sum is taken as
+ * fmaf in ascending pick order from +0.0f (the pages fix no arithmetic; the
+ * two-phase form with the flag hand-off is ll_moe_combine_send / _recv).
  *   layout:       device, as for dispatch (only the signal words of set
  *                 1-parity are written: zeroed).
  *   expert_out:   device, bf16 [num_experts * max_tokens, hidden], 16-byte
