@@ -234,7 +234,10 @@ def summarize_profiles(args) -> None:
     trace = list(csv.DictReader(open(args.trace.replace("kernel_stats", "kernel_trace"))))
     segs, cur = [], None
     for r in trace:
-        if "spin_kernel" in r["Kernel_Name"]:
+        d_ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        # a hold spins for HOLD_CYCLES (hundreds of microseconds); the empty
+        # launches of the floors are spin kernels of no length
+        if "spin_kernel" in r["Kernel_Name"] and d_ns > 50_000:
             cur = {}
             segs.append(cur)
         elif cur is not None:
@@ -249,7 +252,14 @@ def summarize_profiles(args) -> None:
             merged.setdefault(title, {}).setdefault(name, []).extend(ds)
     lines += ["", "## The same launches by timed region of bench.py", "",
               "Each region starts after a stream hold (a spin kernel), queued behind two "
-              "signal-word cleans (not listed).", "",
+              "signal-word cleans (not listed), and runs to the next hold: the timed launches "
+              "are the region's own kernel, but untimed work queued after them (warm-up "
+              "steps, status checks, output fills) is listed under the same region. A receiver "
+              "launched on a second stream before the hold ends waits out the hold, and its "
+              "duration includes that wait. The tracer adds about 3 us to every launch (an "
+              "empty launch back to back: 4.7 us traced, 1.6 us not), so launches of a few "
+              "microseconds run launch-bound here; the kernel durations of the long and the "
+              "dominant kernels agree with bench.py's event timings.", "",
               "| region | kernel | calls | average us |", "|---|---|---|---|"]
     for title, seg in merged.items():
         for name, ds in seg.items():
