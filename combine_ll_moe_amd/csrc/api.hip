@@ -114,27 +114,33 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   // Launch shape: 256-thread workgroups, one token per workgroup up to
   // kDispatchTileBlocks of them, then two. A small batch shares each token's
   // rows among `groups` workgroups, so that the launch has ~512 workgroups:
-  // each builds the whole message and writes its rows. A group needs at
-  // least two rows: more groups than that add atomic instructions on the
-  // signal lines (128 tokens over 8 experts, whose words share one line:
-  // 6.0 us with two rows per group against 4.6 with three). Rows go out by
-  // wavefront (each written whole by one wavefront), except for bf16
-  // messages shared among groups, which go out by group (each row by all
-  // the group's threads, the send row split among the groups): measured
-  // 5.85 against 6.13 us for 128 tokens of 7168 columns, where the fp8
-  // message of the same batch is the other way round (5.70 against 6.19).
+  // each loads (fp8: quantizes) the whole row of x and writes its rows. A
+  // group needs at least two rows: more groups than that add atomic
+  // instructions on the signal lines (128 tokens over 8 experts, whose
+  // words share one line: 6.0 us with two rows per group against 4.6 with
+  // three); with rows from registers 4 groups stay best for 128 tokens of
+  // 7168 columns (bf16 5.51 us against 5.66 with 2 or 3, fp8 5.48 against
+  // 5.53-5.56). Dispatches of 64 MiB or more build the messages in LDS;
+  // their rows go out by wavefront (each written whole by one wavefront),
+  // except for bf16 messages shared among groups, which go out by group
+  // (each row by all the group's threads, the send row split among the
+  // groups), measured 5.85 against 6.13 us through LDS for 128 tokens of
+  // 7168 columns, where the fp8 message is the other way round (5.70
+  // against 6.19).
   int groups = num_tokens > 0 ? kTargetBlocks / num_tokens : 1;
   if (groups > (topk + 1) / 2) groups = (topk + 1) / 2;
   p.groups = groups < 1 ? 1 : groups;
   p.group_rows = dtype == kBf16 && p.groups > 1;
   p.tile = tile_for(num_tokens, p.groups, topk, kDispatchTileBlocks);
+  p.block = kDispatchBlock;
   p.msg_bytes = (uint32_t)L.dispatch_msg;
   p.msg_stride = ((uint32_t)kMsgLdsOffset + p.msg_bytes + 15u) & ~15u;
   // every message of a tile sits in LDS at once
   if ((uint64_t)p.tile * p.msg_stride > dispatch_lds_budget(num_experts)) p.tile = 1;
-  // Large dispatches write mostly to HBM, where whole-line stores pay off;
-  // smaller ones stay in L2 and MALL, where the plain mapping is a little
-  // faster (3% at 16 MB, 24% the other way at 132 MB).
+  // Large dispatches write mostly to HBM, where aligned whole-line stores
+  // from LDS pay off; smaller ones stay in L2 and MALL, where stores straight
+  // from registers at the rows' own phase are faster (see
+  // dispatch_direct_kernel).
   p.line_align = (uint64_t)num_tokens * (uint64_t)(topk + 1) * L.dispatch_msg >= kStreamRowsBytes;
   p.wide_idx = wide_idx_for(topk_idx, num_tokens, topk);
   return from_hip(launch_dispatch(p, dtype, stream));

@@ -12,20 +12,25 @@
 //  - A workgroup (256 threads) takes a tile of consecutive tokens (usually
 //    one) and a group of its destination rows; `groups` workgroups share a
 //    tile (small batches: so that a launch has ~512 workgroups), each
-//    building the tile's messages in LDS (bf16: a 16-byte-aligned copy of
-//    the row; fp8: quantized there) while the routing prologue (route.h)
-//    computes the tile's slots.
-//  - Destination rows (the send row and one receive row per routed pick)
-//    go out from LDS. With wavefront rows each row is written whole by one
-//    wavefront; with group rows (bf16 messages shared among several groups)
-//    every row of the group is written by all its threads in turn, and the
-//    send row is split among the groups. Either way a receive row belongs
-//    to one group, so that group's count follows whole messages. Message rows are
-//    4 + 2h bytes apart, so a destination starts at any 4-byte phase.
-//    Stores are aligned to the destination instead: 0-3 head dwords, then
-//    whole 16-byte chunks, then 0-3 tail dwords; the LDS side absorbs the
-//    phase (dword-granular LDS reads). Large dispatches deal the chunks to
+//    loading the tile's rows of x (fp8: and quantizing them) while the
+//    routing prologue (route.h) computes the tile's slots.
+//  - Dispatches below 64 MiB (dispatch_direct_kernel): every thread writes
+//    the chunks it loaded (fp8: their codes) straight from its registers
+//    to each of its group's rows, with dword-aligned stores at the row's
+//    own 4-byte phase; no LDS copy, no barrier before the stores.
+//  - Larger dispatches (dispatch_kernel): the tile's messages are built in
+//    LDS and the destination rows (the send row and one receive row per
+//    routed pick) go out from there. With wavefront rows each row is
+//    written whole by one wavefront; with group rows (bf16 messages shared
+//    among several groups) every row of the group is written by all its
+//    threads in turn, and the send row is split among the groups. Message
+//    rows are 4 + 2h bytes apart, so a destination starts at any 4-byte
+//    phase. These stores are aligned to the destination: 0-3 head dwords,
+//    then whole 16-byte chunks, then 0-3 tail dwords; the LDS side absorbs
+//    the phase (dword-granular LDS reads), and the chunks are dealt to
 //    lanes by whole 128-byte cache lines (copy_row_wave).
+//  - Either way a receive row belongs to one group, so that group's count
+//    follows whole messages.
 //  - Messages are written with device-coherent (write-through) stores.
 //    Every wavefront waits for its own stores; after a workgroup barrier
 //    wavefront 0 adds one per routed pick of the group to that expert's
@@ -118,56 +123,55 @@ __device__ __forceinline__ uint32_t e4m3_code4_in_range(float p0, float p1, floa
   return (uint32_t)w;
 }
 
-// Codes and scale of unit u (eight elements) of the fp8 message, given its
-// block's inv and scale. IN_RANGE: the products are known to be numbers
-// below 464 in magnitude (see quantize_rounds).
+// The eight codes of one unit (eight elements) of the fp8 message, given
+// its block's inv. IN_RANGE: the products are known to be numbers below 464
+// in magnitude (see quantize_plan).
 template <bool IN_RANGE>
-__device__ __forceinline__ void quantize_unit(uint8_t* msg, int hidden, int u, const u32x4 raw,
-                                              float inv, float scale) {
+__device__ __forceinline__ uint2 quantize_codes(const u32x4 raw, float inv) {
   const float f[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-  uint32_t lo, hi;
-  if constexpr (IN_RANGE) {
-    lo = e4m3_code4_in_range(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-    hi = e4m3_code4_in_range(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-  } else {
-    lo = e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-    hi = e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-  }
-  *reinterpret_cast<uint2*>(msg + 4 + 8 * u) = make_uint2(lo, hi);
-  if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = scale;
+  if constexpr (IN_RANGE)
+    return make_uint2(e4m3_code4_in_range(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                      e4m3_code4_in_range(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
+  else
+    return make_uint2(e4m3_code4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                      e4m3_code4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
 }
 
-// Block inverses and scales of four rounds of units, and whether the
-// wavefront takes the conversion without clamp and NaN patch (wave-uniform).
+// Block inverses and scales of NS (1, 2 or 4) rounds of units, and whether
+// the wavefront takes the conversion without clamp and NaN patch
+// (wave-uniform).
 struct QuantPlan {
   float inv[4];
   float scale[4];
   bool fast;
 };
 
-// The plan of four rounds of units, u0 + s * blockDim for s = 0..3 (all
-// threads call it). A 128-element block is 16 consecutive lanes, one DPP
-// row; the row reduces amax with four DPP steps (swap pairs, swap halves of
-// quads, mirror halves of the row, mirror the row). The two divisions are
-// then made once per lane instead of once per round: lane j of every quad
-// divides for round j, and round s takes its block's inv and scale from
-// lane s of the quad (DPP quad_perm [s,s,s,s]). Every lane of a row holds
-// the same amax, so each quad has all four.
-__device__ __forceinline__ QuantPlan quantize_plan(const u32x4 (&raw)[4]) {
-  uint32_t m[4];
+// The plan of NS rounds of units, u0 + s * blockDim for s < NS (all threads
+// call it). A 128-element block is 16 consecutive lanes, one DPP row; the
+// row reduces amax with four DPP steps (swap pairs, swap halves of quads,
+// mirror halves of the row, mirror the row). The two divisions are then
+// made once per lane instead of once per round: lane j of every quad
+// divides for round j mod NS, and round s takes its block's inv and scale
+// from lane s of the quad (DPP quad_perm [s,s,s,s]). Every lane of a row
+// holds the same amax, so each quad has all NS.
+template <int NS>
+__device__ __forceinline__ QuantPlan quantize_plan(const u32x4 (&raw)[NS]) {
+  static_assert(NS == 1 || NS == 2 || NS == 4, "rounds per quad lane");
+  uint32_t m[NS];
+  uint32_t mm = 0;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) m[s] = max_mag_bits(raw[s]);
-  const uint32_t mm = (m[0] > m[1] ? m[0] : m[1]) > (m[2] > m[3] ? m[2] : m[3])
-                          ? (m[0] > m[1] ? m[0] : m[1])
-                          : (m[2] > m[3] ? m[2] : m[3]);
+  for (int s = 0; s < NS; ++s) {
+    m[s] = max_mag_bits(raw[s]);
+    mm = m[s] > mm ? m[s] : mm;
+  }
   if (__builtin_expect(__ballot(mm > 0x7F80u) != 0, 0)) {  // a NaN in the wave: rare
 #pragma unroll
-    for (int s = 0; s < 4; ++s) m[s] = max_mag_bits_no_nan(raw[s]);
+    for (int s = 0; s < NS; ++s) m[s] = max_mag_bits_no_nan(raw[s]);
   }
-  float amax[4];
+  float amax[NS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < NS; ++s) {
     uint32_t v = m[s];
     v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
     v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -175,8 +179,10 @@ __device__ __forceinline__ QuantPlan quantize_plan(const u32x4 (&raw)[4]) {
     v = dpp_umax<0x140>(v);  // row_mirror
     amax[s] = __uint_as_float(v << 16);
   }
-  const int j = threadIdx.x & 3;
-  const float a = j == 0 ? amax[0] : j == 1 ? amax[1] : j == 2 ? amax[2] : amax[3];
+  const int j = threadIdx.x & (NS - 1);
+  float a = amax[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) a = j == s ? amax[s] : a;
   float inv = 0.0f, scale = 0.0f;
   if (a > 0.0f) {
     inv = 448.0f / a;
@@ -184,41 +190,70 @@ __device__ __forceinline__ QuantPlan quantize_plan(const u32x4 (&raw)[4]) {
   }
   QuantPlan p;
   p.inv[0] = dpp_f32<0x00>(inv);
-  p.inv[1] = dpp_f32<0x55>(inv);
-  p.inv[2] = dpp_f32<0xAA>(inv);
-  p.inv[3] = dpp_f32<0xFF>(inv);
   p.scale[0] = dpp_f32<0x00>(scale);
-  p.scale[1] = dpp_f32<0x55>(scale);
-  p.scale[2] = dpp_f32<0xAA>(scale);
-  p.scale[3] = dpp_f32<0xFF>(scale);
+  if constexpr (NS > 1) {
+    p.inv[1] = dpp_f32<0x55>(inv);
+    p.scale[1] = dpp_f32<0x55>(scale);
+  }
+  if constexpr (NS > 2) {
+    p.inv[2] = dpp_f32<0xAA>(inv);
+    p.inv[3] = dpp_f32<0xFF>(inv);
+    p.scale[2] = dpp_f32<0xAA>(scale);
+    p.scale[3] = dpp_f32<0xFF>(scale);
+  }
   // A block with a finite amax, a finite inv and no NaN in this lane gives
   // products of magnitude at most 448 * (1 + 2^-23): every |x| <= amax and
   // inv is 448 / amax rounded once. Such waves skip the clamp and the NaN
   // patch; a wave with any other block keeps them.
   bool special = mm > 0x7F80u;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < NS; ++s)
     special = special || amax[s] == __builtin_inff() || p.inv[s] == __builtin_inff();
   p.fast = __ballot(special) == 0;
   return p;
 }
 
-// Round s of a plan: unit u0 + s * blockDim (if below the row's units).
+// Codes of round s of a plan (wave-uniform choice of the encoder form).
+__device__ __forceinline__ uint2 quantize_round_codes(const u32x4 raw, const QuantPlan& p, int s) {
+  return __builtin_expect(p.fast, 1) ? quantize_codes<true>(raw, p.inv[s])
+                                     : quantize_codes<false>(raw, p.inv[s]);
+}
+
+// Round s of a plan into an LDS message: unit u0 + s * blockDim (if below
+// the row's units), its codes and, from the block's first unit, its scale.
 __device__ __forceinline__ void quantize_round(uint8_t* msg, int hidden, int u0, int s,
                                                const u32x4 raw, const QuantPlan& p) {
   const int u = u0 + s * (int)blockDim.x;
   if (u >= hidden / 8) return;
-  if (__builtin_expect(p.fast, 1))
-    quantize_unit<true>(msg, hidden, u, raw, p.inv[s], p.scale[s]);
-  else
-    quantize_unit<false>(msg, hidden, u, raw, p.inv[s], p.scale[s]);
+  *reinterpret_cast<uint2*>(msg + 4 + 8 * u) = quantize_round_codes(raw, p, s);
+  if ((u & 15) == 0) *reinterpret_cast<float*>(msg + 4 + hidden + 4 * (u >> 4)) = p.scale[s];
+}
+
+// NS rounds of units quantized into registers: codes of unit
+// u0 + s * blockDim in code[s], its block's scale in scale[s] (all threads
+// call it; units past the end are computed and not used).
+template <int NS>
+struct Fp8Regs {
+  uint2 code[NS];
+  float scale[NS];
+};
+template <int NS>
+__device__ __forceinline__ Fp8Regs<NS> quantize_regs(const u32x4 (&raw)[NS]) {
+  const QuantPlan p = quantize_plan<NS>(raw);
+  Fp8Regs<NS> q;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    q.code[s] = quantize_round_codes(raw[s], p, s);
+    q.scale[s] = p.scale[s];
+  }
+  return q;
 }
 
 // Four rounds of units, u0 + s * blockDim for s = 0..3 (all threads call
 // it; units past the end are computed and not stored).
 __device__ __forceinline__ void quantize_rounds(uint8_t* msg, int hidden, int u0,
                                                 const u32x4 (&raw)[4]) {
-  const QuantPlan p = quantize_plan(raw);
+  const QuantPlan p = quantize_plan<4>(raw);
 #pragma unroll
   for (int s = 0; s < 4; ++s) quantize_round(msg, hidden, u0, s, raw[s], p);
 }
@@ -403,6 +438,147 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   }
 }
 
+// The dispatch with rows straight from registers, for dispatches below
+// the whole-line size (their rows stay in L2 and MALL). Every thread keeps
+// the 16-byte chunks of x it loaded (fp8: their codes and block scales) in
+// registers and writes them to each of its group's rows itself: payload
+// chunk u of a row at byte 4 + 16u (bf16) or codes at 4 + 8u and the block
+// scale after the codes (fp8), dword-aligned buffer stores at whatever
+// 4-byte phase the row has. There is no LDS copy of the message and no
+// barrier before the stores; a row's stores start as soon as the slots are
+// known. (128 tokens of 7168 columns dispatched in 5.51 us against 5.89
+// through LDS, fp8 5.48 against 5.61, 512 tokens of 4096 columns 12.2
+// against 12.8; for rows that go to HBM the straddled 128-byte lines cost
+// more than the LDS round trip: the stores alone of 1024 such tokens took
+// 24.5 us against 21.7 with whole-line stores, so large dispatches keep
+// dispatch_kernel. Workgroups of 512 or 1024 threads, fewer rounds of
+// quantization per thread, measured no faster.)
+//
+// Rows: group g of a tile writes the receive rows of the picks k = g,
+// g + groups, ... and part g of groups of every send row (whole 128-element
+// blocks for fp8, with their scales), each row by all its threads, so a
+// count raised by the group follows whole messages. Tokens of a tile, and
+// rows wider than one round of 4 * 256 chunks, go round by round; each
+// round's loads are issued before the previous round's stores.
+template <int DT, int VEC, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) dispatch_direct_kernel(const DispatchParams P) {
+  extern __shared__ int hist[];  // hist_cap_for(num_experts) ints
+  __shared__ RouteShared rs;
+
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int e = tid; e < P.num_experts; e += BLOCK) P.sig_other[e] = 0;
+
+  // workgroup -> (tile of tokens [t0, t1), row group g), as dispatch_kernel
+  const int xcd = blockIdx.x % kXcds;
+  const int pos = blockIdx.x / kXcds;
+  const int tile = xcd + kXcds * (pos / P.groups);
+  const int g = pos - (pos / P.groups) * P.groups;
+  const int t0 = tile * P.tile;
+  if (t0 >= P.num_tokens) return;
+  const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
+  const int K = P.topk;
+  const int G = P.groups;
+  const int units = P.hidden / 8;  // 16-byte chunks of x (fp8: 8-byte code groups)
+  const uint32_t md = P.msg_bytes;
+  const u32x4* x = reinterpret_cast<const u32x4*>(P.x);
+  // the group's part of the send row, in units
+  const int gran = DT == kBf16 ? 1 : 16;
+  const int parts = units / gran;
+  const int lo = gran * (parts * g / G);
+  const int hi = gran * (parts * (g + 1) / G);
+
+  // units per thread and round: 1024 units (8192 columns) per round
+  constexpr int kStage = BLOCK == 256 ? 4 : BLOCK == 512 ? 2 : 1;
+  static_assert(kStage * BLOCK == 1024, "workgroups of 256, 512 or 1024 threads");
+  constexpr int kRound = kStage * BLOCK;
+  u32x4 r[kStage];
+  Fp8Regs<kStage> q;
+  const int wslot = route_tile<VEC, true>(
+      P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs, hist, hist_cap_for(P.num_experts),
+      [&]() { load_row<kStage>(r, x + (size_t)t0 * units, units); },
+      [&]() {
+        if constexpr (DT == kFp8) q = quantize_regs<kStage>(r);
+      });
+
+  // this thread's units of one round into a row
+  auto put_units = [&](BufRsrc rsrc, int base, int ulo, int uhi) {
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const int u = base + tid + s * BLOCK;
+      if (u < ulo || u >= uhi) continue;
+      if constexpr (DT == kBf16) {
+        store_b128(u32x4_a4{r[s].x, r[s].y, r[s].z, r[s].w}, rsrc, 4u + 16u * (uint32_t)u);
+      } else {
+        store_b64(q.code[s], rsrc, 4u + 8u * (uint32_t)u);
+        if ((u & 15) == 0)
+          store_b32(__float_as_uint(q.scale[s]), rsrc,
+                    4u + (uint32_t)P.hidden + 4u * (uint32_t)(u >> 4));
+      }
+    }
+  };
+  int i = 0;
+  int base = 0;
+  while (true) {  // uniform: one (token, round) per pass
+    int ni = i, nbase = base + kRound;
+    if (nbase >= units) {
+      ni = i + 1;
+      nbase = 0;
+    }
+    const bool more = t0 + ni < t1;
+    u32x4 nx[kStage];
+    if (more) load_row<kStage>(nx, x + (size_t)(t0 + ni) * units, units, nbase);
+
+    const int t = t0 + i;
+    const BufRsrc sr = message_rsrc(P.send + (uint64_t)t * md, md);
+    if (base == 0 && g == 0 && tid == 0) store_b32((uint32_t)t, sr, 0);
+    put_units(sr, base, lo, hi);
+    for (int k = g; k < K; k += G) {
+      const int j = i * K + k;
+      const int slot = __builtin_amdgcn_readlane(wslot, j);
+      if (slot < 0) continue;  // masked
+      const BufRsrc rr = message_rsrc(
+          P.recv + ((uint64_t)rs.expert[j] * (uint64_t)P.max_tokens + (uint64_t)slot) * md, md);
+      if (base == 0 && tid == 0) store_b32((uint32_t)t, rr, 0);
+      put_units(rr, base, 0, units);
+    }
+    if (!more) break;
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) r[s] = nx[s];
+    if constexpr (DT == kFp8) q = quantize_regs<kStage>(r);
+    i = ni;
+    base = nbase;
+  }
+
+  // publish, as dispatch_kernel: every wave's stores complete, one barrier,
+  // then wavefront 0 adds the group's picks in one device-scope atomic
+  // instruction
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid < (t1 - t0) * K) {  // wavefront 0: tile * topk <= 64 entries
+    const int k = tid - (tid / K) * K;
+    if (k - (k / G) * G == g && wslot >= 0)
+      __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + rs.expert[tid]), 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int DT, int VEC, int BLOCK>
+static hipError_t launch_direct_block(const DispatchParams& p, hipStream_t stream) {
+  const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
+  const int rounds = (tiles + kXcds - 1) / kXcds;
+  const size_t lds = sizeof(int) * hist_cap_for(p.num_experts);
+  dispatch_direct_kernel<DT, VEC, BLOCK><<<rounds * kXcds * p.groups, BLOCK, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int DT, int VEC>
+static hipError_t launch_direct(const DispatchParams& p, hipStream_t stream) {
+  if (p.block == 1024) return launch_direct_block<DT, VEC, 1024>(p, stream);
+  if (p.block == 512) return launch_direct_block<DT, VEC, 512>(p, stream);
+  return launch_direct_block<DT, VEC, 256>(p, stream);
+}
+
 template <int DT, bool LINE, int VEC, bool GROUP_ROWS>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
@@ -416,15 +592,14 @@ static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
 
 template <int DT, bool GROUP_ROWS>
 static hipError_t launch_lines(const DispatchParams& p, hipStream_t stream) {
-  if (p.line_align)
-    return p.wide_idx ? launch_dt<DT, true, 4, GROUP_ROWS>(p, stream)
-                      : launch_dt<DT, true, 1, GROUP_ROWS>(p, stream);
-  return p.wide_idx ? launch_dt<DT, false, 4, GROUP_ROWS>(p, stream)
-                    : launch_dt<DT, false, 1, GROUP_ROWS>(p, stream);
+  return p.wide_idx ? launch_dt<DT, true, 4, GROUP_ROWS>(p, stream)
+                    : launch_dt<DT, true, 1, GROUP_ROWS>(p, stream);
 }
 
 template <int DT>
 static hipError_t launch_modes(const DispatchParams& p, hipStream_t stream) {
+  if (!p.line_align)
+    return p.wide_idx ? launch_direct<DT, 4>(p, stream) : launch_direct<DT, 1>(p, stream);
   return p.group_rows ? launch_lines<DT, true>(p, stream) : launch_lines<DT, false>(p, stream);
 }
 

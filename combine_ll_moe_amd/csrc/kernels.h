@@ -25,6 +25,7 @@ struct DispatchParams {
   uint32_t msg_bytes;              // md
   uint32_t msg_stride;             // bytes of one LDS message buffer (one per tile token)
   int line_align;                  // deal store chunks to lanes by whole cache lines
+  int block;                       // threads per workgroup of the register-direct dispatch
   int wide_idx;                    // routing prologue reads 4 entries per load
 };
 

@@ -30,18 +30,25 @@ __device__ __forceinline__ void store_b128(const u32x4_a4 v, BufRsrc r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, POLICY);
 }
 template <int POLICY = kCachePolicySc1>
+__device__ __forceinline__ void store_b64(uint2 v, BufRsrc r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, POLICY);
+}
+template <int POLICY = kCachePolicySc1>
 __device__ __forceinline__ void store_b32(uint32_t v, BufRsrc r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, POLICY);
 }
 
-// The first NSTAGE * blockDim 16-byte chunks of a row into registers;
-// unconditional loads with the index clamped into the row.
+// NSTAGE * blockDim 16-byte chunks of a row into registers, from chunk
+// `base` on (thread i takes chunks base + i + u * blockDim); unconditional
+// loads with the index clamped into the row.
 template <int NSTAGE>
 __device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __restrict__ xr,
-                                         int chunks) {
+                                         int chunks, int base = 0) {
 #pragma unroll
   for (int u = 0; u < NSTAGE; ++u) {
-    const int j = (int)threadIdx.x + u * (int)blockDim.x;
+    const int j = base + (int)threadIdx.x + u * (int)blockDim.x;
     r[u] = xr[j < chunks ? j : chunks - 1];
   }
 }

@@ -94,6 +94,8 @@ def test_ragged_batches(n, dtype):
     (40, 40, 64, 4096, 4, W.BF16),   # largest expert count of the LDS histogram
     (40, 48, 64, 4097, 4, W.BF16),   # ballot path beyond it
     (24, 24, 256, 5000, 12, W.FP8_E4M3),
+    (2048, 2048, 256, 64, 8, W.BF16),    # two-token tiles of rows from registers
+    (2048, 2048, 128, 64, 4, W.FP8_E4M3),
 ])
 @pytest.mark.parametrize("pad", [0, 16, 48])
 def test_shapes_and_base_phases(shape, pad):
@@ -151,6 +153,10 @@ def test_masked_repeated_and_overflowing_picks():
     (32, 32, 43648, 8, 2, W.FP8_E4M3),
     (1024, 1024, 43648, 8, 2, W.FP8_E4M3),
     (2048, 2048, 43648, 8, 2, W.FP8_E4M3),
+    # whole-line stores with a token's rows shared by two workgroups: bf16
+    # rows by workgroup, fp8 rows by wavefront
+    (200, 200, 22520, 64, 8, W.BF16),
+    (200, 200, 43648, 64, 8, W.FP8_E4M3),
 ])
 def test_largest_messages(shape):
     n, cap, h, e, k, dt = shape
