@@ -710,9 +710,9 @@ def measure(name: str, args, torch, ll, W) -> dict:
         per = max(1, min(w.topk + 1, nrows // 512))
         line = nrows * md >= 64 << 20  # the dispatch's whole-line rule
 
-        def store_rows(s, wave_rows, policy=ll.PROBE_SC1):
+        def store_rows(s, rows_mode, policy=ll.PROBE_SC1):
             ll.ll_moe_diag_store_rows(lay, rows_q[s & 1][s % len(batches)], nrows, md, per,
-                                      line, wave_rows, policy, sptr)
+                                      line, rows_mode, policy, sptr)
 
         def gather(s):
             _, _, wt = batches[s % len(batches)]
@@ -720,17 +720,23 @@ def measure(name: str, args, torch, ll, W) -> dict:
                                        gather_rows[s % len(batches)], wt, w.num_tokens, w.topk,
                                        out, sptr)
 
-        # the dispatch's two store routines: rows by workgroup, rows by wavefront
+        # the dispatch's store routines: from LDS by workgroup or by
+        # wavefront, and straight from registers
         st_group = clock.per_call("floor: dispatch's stores alone, rows by workgroup "
-                                  "(store_rows probe)", lambda s: store_rows(s, False), args.steps)
+                                  "(store_rows probe)",
+                                  lambda s: store_rows(s, ll.PROBE_ROWS_GROUP), args.steps)
         st_wave = clock.per_call("floor: dispatch's stores alone, rows by wavefront "
-                                 "(store_rows probe)", lambda s: store_rows(s, True), args.steps)
-        best_wave = st_wave <= st_group
-        st_us = min(st_group, st_wave)
+                                 "(store_rows probe)",
+                                 lambda s: store_rows(s, ll.PROBE_ROWS_WAVE), args.steps)
+        st_direct = clock.per_call("floor: dispatch's stores alone, rows from registers "
+                                   "(store_rows probe)",
+                                   lambda s: store_rows(s, ll.PROBE_ROWS_DIRECT), args.steps)
+        st_us, best_rows = min((st_group, ll.PROBE_ROWS_GROUP), (st_wave, ll.PROBE_ROWS_WAVE),
+                               (st_direct, ll.PROBE_ROWS_DIRECT))
         ga_us = clock.per_call("floor: combine's gather alone (gather_rows probe)", gather,
                                args.steps)
         both_us = clock.per_call("floor: store_rows + gather_rows steps",
-                                 lambda s: (store_rows(s, best_wave), gather(s)), args.steps)
+                                 lambda s: (store_rows(s, best_rows), gather(s)), args.steps)
         empty_us = clock.per_call("floor: empty launches", lambda s: torch.cuda._sleep(0),
                                   args.steps)
         # the same stores with other cache policies (context for the
@@ -740,11 +746,12 @@ def measure(name: str, args, torch, ll, W) -> dict:
                            ("sc1_nt", ll.PROBE_SC1_NT)):
             policies[pname] = round(clock.per_call(
                 f"floor: dispatch's stores alone, {pname} stores",
-                lambda s: store_rows(s, best_wave, pol), args.steps), 3)
+                lambda s: store_rows(s, best_rows, pol), args.steps), 3)
         floors = {
             "store_rows_us": round(st_us, 3), "store_rows_bytes": ab["dispatch_writes"],
             "store_rows_by_workgroup_us": round(st_group, 3),
             "store_rows_by_wavefront_us": round(st_wave, 3),
+            "store_rows_from_registers_us": round(st_direct, 3),
             "store_rows_per_workgroup": per,
             "gather_us": round(ga_us, 3), "gather_bytes": ab["combine"],
             "store_then_gather_us_per_step": round(both_us, 3),
@@ -752,7 +759,7 @@ def measure(name: str, args, torch, ll, W) -> dict:
             "store_rows_other_policies_us": policies,
             "step_us_at_60pct": round(ab["total"] / (0.6 * HBM_PEAK_GBS * 1e9) * 1e6, 3)}
         say(f"floors: stores alone {st_group:.2f} (rows by workgroup) / {st_wave:.2f} "
-            f"(by wavefront) us, gather alone {ga_us:.2f} us, both as steps "
+            f"(by wavefront) / {st_direct:.2f} (from registers) us, gather alone {ga_us:.2f} us, both as steps "
             f"{both_us:.2f} us/step, empty launch {empty_us:.2f} us; other store policies "
             f"{policies}")
         del rows_q, gather_rows

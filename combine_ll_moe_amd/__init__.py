@@ -40,6 +40,9 @@ INVALID_USAGE = 5
 PROBE_WRITE = 0
 PROBE_READ = 1
 PROBE_COPY = 2
+PROBE_ROWS_GROUP = 0
+PROBE_ROWS_WAVE = 1
+PROBE_ROWS_DIRECT = 2
 PROBE_SC1 = 0
 PROBE_WRITE_BACK = 1
 PROBE_NT = 2
@@ -198,10 +201,11 @@ def ll_moe_diag_stream(mode: int, non_temporal: bool, dst, src, nbytes: int, blo
 
 
 def ll_moe_diag_store_rows(base, row_offsets, nrows: int, row_bytes: int, rows_per_block: int,
-                           line: bool, wave_rows: bool, policy: int, stream=None) -> None:
-    """Measurement probe: the dispatch's message stores alone, to listed rows."""
+                           line: bool, rows: int, policy: int, stream=None) -> None:
+    """Measurement probe: the dispatch's message stores alone, to listed rows
+    (rows: PROBE_ROWS_GROUP, PROBE_ROWS_WAVE or PROBE_ROWS_DIRECT)."""
     _check(_lib.ll_moe_diag_store_rows(_ptr(base), _ptr(row_offsets), nrows, row_bytes,
-                                       rows_per_block, int(bool(line)), int(bool(wave_rows)),
+                                       rows_per_block, int(bool(line)), int(rows),
                                        policy, _stream(stream)), "ll_moe_diag_store_rows")
 
 

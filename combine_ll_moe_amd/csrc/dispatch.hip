@@ -503,13 +503,13 @@ __global__ void __launch_bounds__(BLOCK) dispatch_direct_kernel(const DispatchPa
 
   // this thread's units of one round into a row
   auto put_units = [&](BufRsrc rsrc, int base, int ulo, int uhi) {
+    if constexpr (DT == kBf16) {
+      put_chunks<kStage, BLOCK>(rsrc, r, base, ulo, uhi);
+    } else {
 #pragma unroll
-    for (int s = 0; s < kStage; ++s) {
-      const int u = base + tid + s * BLOCK;
-      if (u < ulo || u >= uhi) continue;
-      if constexpr (DT == kBf16) {
-        store_b128(u32x4_a4{r[s].x, r[s].y, r[s].z, r[s].w}, rsrc, 4u + 16u * (uint32_t)u);
-      } else {
+      for (int s = 0; s < kStage; ++s) {
+        const int u = base + tid + s * BLOCK;
+        if (u < ulo || u >= uhi) continue;
         store_b64(q.code[s], rsrc, 4u + 8u * (uint32_t)u);
         if ((u & 15) == 0)
           store_b32(__float_as_uint(q.scale[s]), rsrc,

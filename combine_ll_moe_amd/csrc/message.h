@@ -1,7 +1,8 @@
 // Message movement shared by the kernels that write messages for another
 // workgroup or kernel to read (dispatch, two-phase combine expert side):
-// register loads of a 16-byte-aligned row, and the copy of a message from
-// LDS to its destination with device-coherent stores.
+// register loads of a 16-byte-aligned row, and the stores of a message to
+// its destination with device-coherent stores, from registers or from an
+// LDS copy.
 //
 // Message stores are buffer stores with the device-scope coherence bit
 // (sc1): they write through the XCD's L2, so they are visible to every XCD
@@ -50,6 +51,24 @@ __device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __rest
   for (int u = 0; u < NSTAGE; ++u) {
     const int j = base + (int)threadIdx.x + u * (int)blockDim.x;
     r[u] = xr[j < chunks ? j : chunks - 1];
+  }
+}
+
+// Payload chunks of one round straight from registers into a message row:
+// thread i holds chunks base + i + s * BLOCK (s < NS) in r[s] and stores
+// those within [lo, hi) at row byte 4 + 16 * chunk, after the 4-byte
+// header. The stores are 16-byte buffer stores at whatever 4-byte phase
+// the row has (dword-aligned), of the given cache policy, confined to the
+// message by the buffer descriptor; there is no LDS copy of the row.
+template <int NS, int BLOCK, int POLICY = kCachePolicySc1>
+__device__ __forceinline__ void put_chunks(BufRsrc rsrc, const u32x4 (&r)[NS], int base, int lo,
+                                           int hi) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int c = base + tid + s * BLOCK;
+    if (c >= lo && c < hi)
+      store_b128<POLICY>(u32x4_a4{r[s].x, r[s].y, r[s].z, r[s].w}, rsrc, 4u + 16u * (uint32_t)c);
   }
 }
 

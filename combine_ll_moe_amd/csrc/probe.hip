@@ -5,11 +5,12 @@
 //  - stream: a contiguous write, read or copy of a large buffer, 16-byte
 //    accesses, four in flight per thread: the practical HBM ceilings.
 //  - store_rows: the dispatch's stores alone. Every listed destination row
-//    receives row_bytes bytes from an LDS buffer through one of the
-//    dispatch's own store routines (rows by workgroup, copy_message, or by
-//    wavefront, copy_row_wave: destination-aligned 16-byte buffer stores,
-//    optionally whole-line dealing), with no loads of x, no routing and no
-//    count publish.
+//    receives row_bytes bytes of a pattern through one of the dispatch's
+//    own store routines: from an LDS buffer by workgroup (copy_message) or
+//    by wavefront (copy_row_wave), destination-aligned 16-byte buffer
+//    stores, optionally whole-line dealing; or straight from registers
+//    (put_chunks, as the dispatch writes batches below 64 MiB). No loads of
+//    x, no routing and no count publish.
 //  - gather_rows: the combine's gather alone. Each token folds the listed
 //    expert-output rows through the combine's own gather_fold, in the
 //    combine's launch shape, with no routing prologue.
@@ -118,6 +119,59 @@ __global__ void __launch_bounds__(kProbeBlock)
   }
 }
 
+// Rows straight from registers: workgroup b writes rows [b * per, (b + 1)
+// * per) of the list, each by all its threads, the pattern computed in
+// registers round by round (rows of a 4-byte header and whole 16-byte
+// chunks).
+template <int POLICY>
+__global__ void __launch_bounds__(kProbeBlock)
+    store_rows_direct_kernel(uint8_t* base, const int64_t* __restrict__ off, int nrows,
+                             uint32_t row_bytes, int per) {
+  constexpr int kStage = 4;
+  constexpr int kRound = kStage * kProbeBlock;
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * per;
+  const int r1 = r0 + per < nrows ? r0 + per : nrows;
+  const int chunks = (int)((row_bytes - 4u) / 16u);
+  for (int cb = 0; cb < chunks; cb += kRound) {  // uniform
+    u32x4 v[kStage];
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const uint32_t b = 4u + 16u * (uint32_t)(cb + tid + s * kProbeBlock);
+      v[s] = u32x4{0xC3C30000u ^ b, 0xC3C30000u ^ (b + 4u), 0xC3C30000u ^ (b + 8u),
+                   0xC3C30000u ^ (b + 12u)};
+    }
+    for (int r = r0; r < r1; ++r) {
+      const BufRsrc rs = message_rsrc(base + off[r], row_bytes);
+      if (cb == 0 && tid == 0) store_b32<POLICY>(0xC3C30000u, rs, 0);
+      put_chunks<kStage, kProbeBlock, POLICY>(rs, v, cb, 0, chunks);
+    }
+  }
+}
+
+hipError_t launch_store_rows_direct(int policy, uint8_t* base, const int64_t* off, int nrows,
+                                    uint32_t row_bytes, int per, hipStream_t stream) {
+  const int blocks = (nrows + per - 1) / per;
+#define LLMOE_STORE_DIRECT(POL) \
+  store_rows_direct_kernel<POL><<<blocks, kProbeBlock, 0, stream>>>(base, off, nrows, row_bytes, per)
+  switch (policy) {
+    case LL_MOE_PROBE_SC1:
+      LLMOE_STORE_DIRECT(kCachePolicySc1);
+      break;
+    case LL_MOE_PROBE_WRITE_BACK:
+      LLMOE_STORE_DIRECT(0);
+      break;
+    case LL_MOE_PROBE_NT:
+      LLMOE_STORE_DIRECT(kCachePolicyNt);
+      break;
+    default:
+      LLMOE_STORE_DIRECT(kCachePolicySc1 | kCachePolicyNt);
+      break;
+  }
+#undef LLMOE_STORE_DIRECT
+  return hipGetLastError();
+}
+
 template <bool LINE, bool WAVE_ROWS>
 hipError_t launch_store_rows_policy(int policy, uint8_t* base, const int64_t* off, int nrows,
                                     uint32_t row_bytes, int per, hipStream_t stream) {
@@ -224,29 +278,35 @@ extern "C" int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const v
 }
 
 extern "C" int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows,
-                                      int row_bytes, int rows_per_block, int line, int wave_rows,
+                                      int row_bytes, int rows_per_block, int line, int rows,
                                       int policy, hipStream_t stream) {
   if (nrows < 0 || row_bytes < 4 || row_bytes % 4 != 0 ||
       (uint64_t)row_bytes > kMaxMessageBytes)
     return LL_MOE_INVALID_ARGUMENT;
   if (rows_per_block < 1 || rows_per_block > kMaxRowsPerBlock) return LL_MOE_INVALID_ARGUMENT;
   if (policy < LL_MOE_PROBE_SC1 || policy > LL_MOE_PROBE_SC1_NT) return LL_MOE_INVALID_ARGUMENT;
+  if (rows < LL_MOE_PROBE_ROWS_GROUP || rows > LL_MOE_PROBE_ROWS_DIRECT)
+    return LL_MOE_INVALID_ARGUMENT;
+  if (rows == LL_MOE_PROBE_ROWS_DIRECT && (row_bytes - 4) % 16 != 0) return LL_MOE_INVALID_ARGUMENT;
   if (nrows == 0) return LL_MOE_SUCCESS;
   if (!base || !row_offsets || !aligned(base, 16) || !aligned(row_offsets, 8))
     return LL_MOE_INVALID_ARGUMENT;
   uint8_t* b = static_cast<uint8_t*>(base);
   const uint32_t rb = (uint32_t)row_bytes;
+  const bool wave = rows == LL_MOE_PROBE_ROWS_WAVE;
   hipError_t e;
-  if (line)
-    e = wave_rows ? launch_store_rows_policy<true, true>(policy, b, row_offsets, nrows, rb,
-                                                         rows_per_block, stream)
-                  : launch_store_rows_policy<true, false>(policy, b, row_offsets, nrows, rb,
-                                                          rows_per_block, stream);
+  if (rows == LL_MOE_PROBE_ROWS_DIRECT)
+    e = launch_store_rows_direct(policy, b, row_offsets, nrows, rb, rows_per_block, stream);
+  else if (line)
+    e = wave ? launch_store_rows_policy<true, true>(policy, b, row_offsets, nrows, rb,
+                                                    rows_per_block, stream)
+             : launch_store_rows_policy<true, false>(policy, b, row_offsets, nrows, rb,
+                                                     rows_per_block, stream);
   else
-    e = wave_rows ? launch_store_rows_policy<false, true>(policy, b, row_offsets, nrows, rb,
-                                                          rows_per_block, stream)
-                  : launch_store_rows_policy<false, false>(policy, b, row_offsets, nrows, rb,
-                                                           rows_per_block, stream);
+    e = wave ? launch_store_rows_policy<false, true>(policy, b, row_offsets, nrows, rb,
+                                                     rows_per_block, stream)
+             : launch_store_rows_policy<false, false>(policy, b, row_offsets, nrows, rb,
+                                                      rows_per_block, stream);
   return from_hip(e);
 }
 

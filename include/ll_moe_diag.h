@@ -112,27 +112,40 @@ int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const void* src, s
 #define LL_MOE_PROBE_NT 2          /* non-temporal */
 #define LL_MOE_PROBE_SC1_NT 3      /* write-through and non-temporal */
 
+/* Store routines of ll_moe_diag_store_rows. */
+#define LL_MOE_PROBE_ROWS_GROUP 0   /* from LDS, each row by all threads in turn */
+#define LL_MOE_PROBE_ROWS_WAVE 1    /* from LDS, each row whole by one wavefront */
+#define LL_MOE_PROBE_ROWS_DIRECT 2  /* from registers, each row by all threads */
+
 /*
  * ll_moe_diag_store_rows — the dispatch's message stores alone: row i of
- * the list receives row_bytes bytes of a pattern at base + row_offsets[i],
- * from an LDS buffer, through one of the dispatch's store routines
- * (destination-aligned 16-byte buffer stores of the given policy; with
- * line != 0 the chunks are dealt to lanes by whole 128-byte lines, as the
- * dispatch does for its largest batches). Workgroup b (256 threads) writes
- * rows [b * rows_per_block, (b + 1) * rows_per_block): with wave_rows == 0
- * every row by all its threads in turn, with wave_rows != 0 each row whole
- * by one wavefront (wavefront w: rows w, w + 4, ...). No other loads, no
- * counts.
+ * the list receives row_bytes bytes of a pattern at base + row_offsets[i]
+ * through one of the dispatch's store routines, with stores of the given
+ * policy. Workgroup b (256 threads) writes rows [b * rows_per_block,
+ * (b + 1) * rows_per_block):
+ *   rows == LL_MOE_PROBE_ROWS_GROUP: from an LDS buffer, every row by all
+ *     its threads in turn (destination-aligned 16-byte buffer stores);
+ *   rows == LL_MOE_PROBE_ROWS_WAVE: from an LDS buffer, each row whole by
+ *     one wavefront (wavefront w: rows w, w + 4, ...);
+ *   rows == LL_MOE_PROBE_ROWS_DIRECT: straight from registers, every row by
+ *     all its threads, payload chunk c at row byte 4 + 16c (dword-aligned
+ *     16-byte stores at the row's own phase), as the dispatch writes its
+ *     batches below 64 MiB; row_bytes must be 4 more than a multiple of 16
+ *     (a message row).
+ * With line != 0 the LDS routines deal the chunks to lanes by whole
+ * 128-byte lines, as the dispatch does for its largest batches (ignored by
+ * the direct routine). No other loads, no counts.
  *   base:        device, 16-byte aligned.
  *   row_offsets: device, int64 [nrows], each a multiple of 4; every row
  *                [offset, offset + row_bytes) must lie inside base's
  *                allocation (the caller's duty: the probe cannot see it).
  * INVALID_ARGUMENT: nrows < 0, row_bytes not a positive multiple of 4 or
- * above LL_MOE_MAX_MESSAGE_BYTES, rows_per_block outside [1, 256], an
- * unknown policy, a null or misaligned pointer.
+ * above LL_MOE_MAX_MESSAGE_BYTES (direct: not 4 more than a multiple of
+ * 16), rows_per_block outside [1, 256], an unknown routine or policy, a
+ * null or misaligned pointer.
  */
 int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows, int row_bytes,
-                           int rows_per_block, int line, int wave_rows, int policy,
+                           int rows_per_block, int line, int rows, int policy,
                            hipStream_t stream);
 
 /*

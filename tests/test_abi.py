@@ -122,6 +122,20 @@ def test_watch_rejects_bad_arguments(case):
     assert rc == ll.INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", [
+    dict(rows=3), dict(rows=-1), dict(rows=2, row_bytes=2008), dict(row_bytes=2002),
+    dict(per=0), dict(per=257), dict(policy=4), dict(base=0), dict(base=FAKE + 4),
+    dict(offs=FAKE + 4),
+])
+def test_store_probe_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(base=FAKE, offs=FAKE, nrows=3, row_bytes=2004, per=1, line=0, rows=0, policy=0)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_diag_store_rows", a["base"], a["offs"], a["nrows"], a["row_bytes"],
+                       a["per"], a["line"], a["rows"], a["policy"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 BIG = 1 << 36  # far above any FAKE layout: never overlaps it
 
 

@@ -71,20 +71,26 @@ def test_gather_probe_skips_rows_out_of_range():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("line,wave_rows,policy", [(False, False, 0), (True, False, 0),
-                                                   (False, True, 0), (True, True, 0),
-                                                   (False, False, 1), (False, True, 2),
-                                                   (True, False, 3)])
-def test_store_probe_writes_only_its_rows(line, wave_rows, policy):
-    row_bytes = 4 + 2 * 1000  # 4-byte phases, as message rows
+G_, W_, D_ = ll.PROBE_ROWS_GROUP, ll.PROBE_ROWS_WAVE, ll.PROBE_ROWS_DIRECT
+
+
+@pytest.mark.parametrize("line,rows_mode,policy,row_bytes", [
+    (False, G_, 0, 2004), (True, G_, 0, 2004), (False, W_, 0, 2004), (True, W_, 0, 2004),
+    (False, G_, 1, 2004), (False, W_, 2, 2004), (True, G_, 3, 2004),
+    (False, D_, 0, 2004), (False, D_, 1, 2004), (True, D_, 3, 2004),
+    (False, D_, 0, 4 + 16 * 1500),  # two rounds of register chunks
+])
+def test_store_probe_writes_only_its_rows(line, rows_mode, policy, row_bytes):
+    # rows of a 4-byte header and whole 16-byte chunks: 4-byte phases, as
+    # message rows
     nrows, space = 37, 64
     rng = np.random.default_rng(1)
     slots = np.sort(rng.choice(space, nrows, replace=False))
     offs = (slots * row_bytes).astype(np.int64)
     buf = torch.full((space * row_bytes + 64,), 0xA5, dtype=torch.uint8, device=DEV)
     base = buf[16:]
-    say(f"[probe] store_rows line={line} wave_rows={wave_rows} policy={policy}")
-    ll.ll_moe_diag_store_rows(base, to_dev(offs), nrows, row_bytes, 6, line, wave_rows, policy)
+    say(f"[probe] store_rows line={line} rows={rows_mode} policy={policy} row_bytes={row_bytes}")
+    ll.ll_moe_diag_store_rows(base, to_dev(offs), nrows, row_bytes, 6, line, rows_mode, policy)
     torch.cuda.synchronize()
     got = buf.cpu().numpy()
     want = np.full_like(got, 0xA5)
