@@ -366,10 +366,25 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   //    slots in its own lanes.
   constexpr int kStage = 4;
   u32x4 r[kStage];
+  // A bf16 send row that one group writes whole and that fits one round of
+  // registers goes out straight from them as soon as x[t0] is back, before
+  // the routing histogram: the stores start while the prologue runs (1024
+  // tokens of 7168 columns: 26.3 against 26.6 us).
+  constexpr bool kEarlyKind = DT == kBf16 && !GROUP_ROWS;
+  const bool early = kEarlyKind && G == 1 && chunks <= kStage * kDispatchBlock;
   const int wslot = route_tile<VEC, true>(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs,
       reinterpret_cast<int*>(lds_raw + P.tile * P.msg_stride), hist_cap_for(P.num_experts),
-      [&]() { load_row<kStage>(r, x + (size_t)t0 * chunks, chunks); },
+      [&]() {
+        load_row<kStage>(r, x + (size_t)t0 * chunks, chunks);
+        if constexpr (kEarlyKind) {
+          if (early) {
+            const BufRsrc sr = message_rsrc(P.send + (uint64_t)t0 * md, md);
+            if (tid == 0) store_b32((uint32_t)t0, sr, 0);
+            put_chunks<kStage, kDispatchBlock>(sr, r, 0, 0, chunks);
+          }
+        }
+      },
       [&]() {
         build_message<DT, kStage>(message_buffer(0), t0, x + (size_t)t0 * chunks, P.hidden, r);
       });
@@ -400,6 +415,7 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
       const int i = rho / (K + 1);
       const int m = rho - i * (K + 1);
       if (m == 0) {
+        if (early && i == 0) continue;  // went out from registers
         copy_row_wave<LINE>(P.send + (uint64_t)(t0 + i) * md, message_buffer(i), md);
       } else {
         const int j = i * K + m - 1;
