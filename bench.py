@@ -85,12 +85,16 @@ def unpack_bytes(w, md: int, routed: int) -> int:
     return 8 * e + routed * md + routed * (row + 4) + 4 * e + 8 * e
 
 
-KERNEL_NAMES = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
-                "send": "combine_send_kernel", "recv": "combine_recv_kernel",
-                "unpack": "dispatch_recv_kernel"}
+# kernel names in the traces (a launch matches any of its role's names): the
+# dispatch runs as dispatch_direct_kernel below 64 MiB, dispatch_kernel above
+KERNEL_NAMES = {"dispatch": ("dispatch_kernel<", "dispatch_direct_kernel<"),
+                "combine": ("combine_kernel<",), "send": ("combine_send_kernel",),
+                "recv": ("combine_recv_kernel<",), "unpack": ("dispatch_recv_kernel",)}
 COUNTERS_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                              "hbm_counters.json")
-COPY_KERNEL = "stream_kernel"  # the hand-written copy that calibrates the counters
+# the hand-written copy that calibrates the counters: the stream probe's
+# copy mode (the source is first filled by its write mode)
+COPY_KERNEL = "stream_kernel<2,"
 
 
 # The sources of the dispatch / combine path (launch shapes included); the
@@ -192,9 +196,9 @@ def summarize_profiles(args) -> None:
     copy = {"bytes": args.copy_bytes, "kernel": copy_name,
             "fetch_kib": round(cfetch[copy_name], 1), "write_kib": round(cwrite[copy_name], 1)}
     per = {}
-    for short, name in KERNEL_NAMES.items():
-        fk = [k for k in fetch if name in k and "probe" not in k]
-        wk = [k for k in write if name in k and "probe" not in k]
+    for short, names in KERNEL_NAMES.items():
+        fk = [k for k in fetch if any(n in k for n in names) and "probe" not in k]
+        wk = [k for k in write if any(n in k for n in names) and "probe" not in k]
         if fk and wk:
             per[short] = {"kernel": fk[0], "fetch_kib": round(fetch[fk[0]], 1),
                           "write_kib": round(write[wk[0]], 1)}
