@@ -3,7 +3,10 @@
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload NAME]
 
 A step is one dispatch(q) + one combine(q) over one decode micro-batch, with
-the parity q alternating step by step, all inputs resident in HBM.
+the parity q alternating step by step, all inputs resident in HBM. Before the
+W warm-up steps each workload runs its step untimed for --settle-ms (25 ms)
+so that the part's clocks have settled: after a short warm-up alone the first
+timed region of 1024 tokens ran 2-3% slower than every later one.
 
 With no --workload the run times three workloads in one process, one after
 the other, each layout freed before the next is allocated:
@@ -427,6 +430,16 @@ def measure(name: str, args, torch, ll, W) -> dict:
     clock = Clock(torch, stream, reset_sets)
     say = lambda msg: print(f"[bench {name}] {msg}", file=sys.stderr, flush=True)
 
+    # untimed: steps for settle_ms of wall time (whole pairs of parities),
+    # then the W warm-up steps
+    t_settle = time.perf_counter() + args.settle_ms * 1e-3
+    settle_steps = 0
+    while time.perf_counter() < t_settle:
+        for s in range(20):
+            step(s)
+        torch.cuda.synchronize()
+        settle_steps += 20
+    reset_sets()
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -783,6 +796,7 @@ def measure(name: str, args, torch, ll, W) -> dict:
         "value": round(gbs, 2),
         "fraction_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "kernels_us": {"dispatch": round(d_us, 3), "combine": round(c_us, 3)},
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "graph_us_per_step": None if graph_us is None else round(graph_us, 3),
         "step_trials_us": {"n": len(trials),
                            "median": round(float(np.median(trials)), 3) if trials else None,
@@ -851,6 +865,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=25.0,
+                    help="untimed steps for this long before the warm-up steps (clocks settle)")
     ap.add_argument("--workload", default=None,
                     help="time one workload only (default: worst_fill, decode and decode_fp8, "
                          "worst_fill the headline)")
@@ -946,6 +962,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": h["settle"],
         "ms_per_step": round(h["us_per_step"] * 1e-3, 6),
         "us_per_step": h["us_per_step"],
         "higher_is_better": True,
