@@ -20,11 +20,13 @@
 //    loads all counts and forms their exclusive prefix in LDS, then takes a
 //    contiguous run of rows, 64 at a time. Lane l finds its row's expert by
 //    binary search in the prefix and loads the row's header; then the
-//    workgroup copies the rows one by one through LDS (the source row is
-//    16-byte aligned, the staging row starts at any 4-byte phase, and the
-//    phase is only known once the header is back: the row's loads go out
-//    together with the header load), next row's loads in flight while the
-//    current row is stored. Release as in the dispatch: device-coherent
+//    workgroup copies the rows one by one (the source row is 16-byte
+//    aligned, the staging row starts at any 4-byte phase, and the phase is
+//    only known once the header is back: the row's loads go out together
+//    with the header load), next row's loads in flight while the current
+//    row is stored: straight from registers with dword-aligned stores below
+//    64 MiB of staged rows, through LDS with destination-aligned whole-line
+//    stores above (mostly HBM-bound writes). Release as in the dispatch: device-coherent
 //    stores, each wave waits for its own, a barrier, then wave 0 adds per
 //    distinct expert the rows it staged to the flag with one device-scope
 //    atomic on the word's high half.
@@ -123,6 +125,75 @@ __device__ __forceinline__ void stage_rows(const SendParams& P, uint32_t* pre, u
   }
 }
 
+// The same staging straight from registers, for batches below
+// kSendLineBytes (their rows stay in L2 and MALL): every thread keeps the
+// 16-byte chunks of the output row it loaded and stores them at staging
+// byte 4 + 16c, dword-aligned stores at the row's own 4-byte phase, so no
+// LDS copy and no barrier come between a row's loads and its stores; the
+// next row's loads are issued before the current row's stores.
+__device__ __forceinline__ void stage_rows_direct(const SendParams& P, uint32_t* pre, uint32_t r0,
+                                                  uint32_t r1) {
+  constexpr int kStage = 4;
+  constexpr int kRound = kStage * kSendBlock;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int E = P.num_experts;
+  const int chunks = P.hidden / 8;
+  const uint32_t mc = P.comb_bytes;
+  const u32x4* y = reinterpret_cast<const u32x4*>(P.y);
+
+  for (uint32_t b0 = r0; b0 < r1; b0 += kWave) {
+    const int n = r1 - b0 < (uint32_t)kWave ? (int)(r1 - b0) : kWave;
+    // this lane's row of the batch: expert, slot and header
+    const uint32_t r = b0 + (uint32_t)(lane < n ? lane : n - 1);
+    const int e_l = expert_of_row(pre, E, r);
+    const int j_l = (int)(r - pre[e_l]);
+    const uint64_t src_l = (uint64_t)e_l * (uint64_t)P.max_tokens + (uint64_t)j_l;
+    const int t_l = *reinterpret_cast<const int32_t*>(P.recv + src_l * P.msg_bytes);
+
+    auto src_row = [&](int i) {
+      const int e = __builtin_amdgcn_readlane(e_l, i);
+      const int j = __builtin_amdgcn_readlane(j_l, i);
+      return y + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)j) * (uint64_t)chunks;
+    };
+    u32x4 v[kStage];
+    load_row<kStage>(v, src_row(0), chunks);
+    for (int i = 0; i < n; ++i) {
+      u32x4 nx[kStage];
+      if (i + 1 < n) load_row<kStage>(nx, src_row(i + 1), chunks);
+      const int t = __builtin_amdgcn_readlane(t_l, i);
+      const int e = __builtin_amdgcn_readlane(e_l, i);
+      if (t >= 0 && t < P.max_tokens) {
+        const BufRsrc rsrc = message_rsrc(
+            P.stage + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)t) * mc, mc);
+        if (tid == 0) store_b32((uint32_t)t, rsrc, 0);
+        put_chunks<kStage, kSendBlock>(rsrc, v, 0, 0, chunks);
+        for (int cb = kRound; cb < chunks; cb += kRound) {  // rows wider than one round
+          u32x4 w[kStage];
+          load_row<kStage>(w, src_row(i), chunks, cb);
+          put_chunks<kStage, kSendBlock>(rsrc, w, cb, 0, chunks);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) v[u] = nx[u];
+    }
+
+    // release, as stage_rows
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid < kWave) {
+      const int e = lane < n && t_l >= 0 && t_l < P.max_tokens ? e_l : -1;
+      int group = 0;
+      for_each_distinct(e, [&](int val, uint64_t same) {
+        if (e == val && (same & lanes_below()) == 0) group = __popcll(same);
+      });
+      if (group > 0)
+        __hip_atomic_fetch_add(reinterpret_cast<unsigned int*>(P.sig + e) + 1, (unsigned int)group,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ uint32_t wave_sum[kSendBlock / kWave];
@@ -145,7 +216,7 @@ __global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendPara
   if ((uint64_t)rows * P.comb_bytes >= kSendLineBytes)
     stage_rows<true>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
   else
-    stage_rows<false>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
+    stage_rows_direct(P, pre, r0, r1);
 }
 
 hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stream) {
