@@ -21,10 +21,10 @@ struct DispatchParams {
   int topk;
   int tile;                        // consecutive tokens per workgroup
   int groups;                      // workgroups per tile (each takes every groups-th row)
-  int group_rows;                  // rows written by whole workgroups (else by wavefronts)
+  int group_rows;                  // LDS path: rows by whole workgroups (else by wavefronts)
   uint32_t msg_bytes;              // md
-  uint32_t msg_stride;             // bytes of one LDS message buffer (one per tile token)
-  int line_align;                  // deal store chunks to lanes by whole cache lines
+  uint32_t msg_stride;             // LDS path: bytes of one message buffer (one per tile token)
+  int line_align;                  // 64 MiB of rows or more: the LDS path, whole-line stores
   int block;                       // threads per workgroup of the register-direct dispatch
   int wide_idx;                    // routing prologue reads 4 entries per load
 };
