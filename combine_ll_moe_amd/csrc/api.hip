@@ -291,8 +291,14 @@ extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens,
 
 namespace {
 // Expert side of the dispatch: a fixed grid, one workgroup per CU, so that
-// while it waits beside a running dispatch it leaves the dispatch room.
+// while it waits beside a running dispatch it leaves the dispatch room; two
+// per CU when the step routes 64 MiB of messages or more, whose copy is
+// bandwidth-bound (1024 tokens of 7168 columns: unpack 44.6 against 48.7
+// us, and the dispatch with a receiver waiting beside it 81.3 against 86.3
+// us to the expert inputs; four per CU unpack no faster and slow that
+// dispatch to 86.9).
 constexpr int kUnpackBlocks = 256;
+constexpr int kUnpackWideBlocks = 512;
 }  // namespace
 
 extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, int num_experts,
@@ -339,7 +345,9 @@ extern "C" int ll_moe_dispatch_recv(void* layout, int max_tokens, int hidden, in
   p.row_bytes = (uint32_t)row_bytes;
   p.expected = expected;
   p.max_spins = max_spins;
-  const int blocks = slots < kUnpackBlocks ? (int)slots : kUnpackBlocks;
+  p.wide = (uint64_t)expected * L.dispatch_msg >= kStreamRowsBytes;
+  const int grid = p.wide ? kUnpackWideBlocks : kUnpackBlocks;
+  const int blocks = slots < grid ? (int)slots : grid;
   return from_hip(launch_dispatch_recv(p, blocks, stream));
 }
 

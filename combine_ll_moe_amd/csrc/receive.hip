@@ -35,6 +35,11 @@
 
 namespace llmoe {
 
+// KROUND: 16-byte loads in flight per lane before their stores (16 for
+// the bandwidth-bound copies of 64 MiB or more: 1024 tokens of 7168
+// columns 44.6 against 44.8 us with 8; 8 below, where 16 measured slower,
+// 6.9 against 6.6 us at 128 tokens).
+template <int KROUND>
 __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ uint32_t wave_sum[kSendBlock / kWave];
@@ -110,7 +115,7 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
   const int waves = (int)blockDim.x / kWave;
   const uint32_t nch = P.row_bytes / 16;                 // 16-byte payload chunks per row
   const uint32_t nsc = P.fp8 ? (uint32_t)P.hidden / 128 : 0u;  // scales per row
-  constexpr int kRound = 8;
+  constexpr int kRound = KROUND;
   for (uint32_t b0 = r0; b0 < r1; b0 += kWave) {
     const int n = r1 - b0 < (uint32_t)kWave ? (int)(r1 - b0) : kWave;
     const uint32_t r = b0 + (uint32_t)(lane < n ? lane : n - 1);
@@ -145,7 +150,10 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
 }
 
 hipError_t launch_dispatch_recv(const UnpackParams& p, int blocks, hipStream_t stream) {
-  dispatch_recv_kernel<<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
+  if (p.wide)
+    dispatch_recv_kernel<16><<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
+  else
+    dispatch_recv_kernel<8><<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
   return hipGetLastError();
 }
 

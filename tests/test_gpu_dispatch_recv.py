@@ -179,6 +179,20 @@ def test_unpack_many_rows_per_workgroup():
     _step(st, 0, x, idx)
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP8_E4M3])
+def test_unpack_wide_grid(dtype):
+    """Steps that route 64 MiB of messages or more take the receiver's wider
+    grid and deeper loads: 16384 messages of 4228 (fp8) or 8196 (bf16)
+    bytes, queued and beside a running dispatch."""
+    w = W.Workload("wide", 2048, 4096, 64, 8, dtype, "uniform", max_tokens=2048, seed=21 + dtype)
+    md, _ = oracle.message_bytes(w.hidden, w.dtype)
+    assert w.num_tokens * w.topk * md >= 64 << 20
+    x, idx = W.tokens(w), W.routing(w)
+    st = Step(w, full_image=False)
+    _step(st, 0, x, idx)
+    _step(st, 1, x, idx, overlapped=True)
+
+
 def test_unpack_masked_entries():
     w = W.Workload("masked", 64, 1024, 16, 4, W.FP8_E4M3, "uniform", seed=12)
     x, idx = W.tokens(w), W.routing(w)
