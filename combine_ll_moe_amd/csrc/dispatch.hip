@@ -317,7 +317,7 @@ __device__ __forceinline__ void build_message(uint8_t* msg, int t, const u32x4* 
   }
 }
 
-template <int DT, bool LINE, int VEC, bool GROUP_ROWS>
+template <int DT, int VEC, bool GROUP_ROWS>
 __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const DispatchParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ RouteShared rs;
@@ -400,12 +400,12 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
   if constexpr (GROUP_ROWS) {
     for (int i = 0; i < t1 - t0; ++i) {
       const uint8_t* msg = message_buffer(i);
-      copy_message<LINE>(P.send + (uint64_t)(t0 + i) * md, msg, md, g, G);
+      copy_message<true>(P.send + (uint64_t)(t0 + i) * md, msg, md, g, G);
       for (int k = g; k < K; k += G) {
         const int j = i * K + k;
         const int s = __builtin_amdgcn_readlane(wslot, j);
         if (s < 0) continue;  // masked
-        copy_message<LINE>(
+        copy_message<true>(
             P.recv + ((uint64_t)rs.expert[j] * (uint64_t)P.max_tokens + (uint64_t)s) * md, msg, md);
       }
     }
@@ -416,12 +416,12 @@ __global__ void __launch_bounds__(kDispatchBlock) dispatch_kernel(const Dispatch
       const int m = rho - i * (K + 1);
       if (m == 0) {
         if (early && i == 0) continue;  // went out from registers
-        copy_row_wave<LINE>(P.send + (uint64_t)(t0 + i) * md, message_buffer(i), md);
+        copy_row_wave<true>(P.send + (uint64_t)(t0 + i) * md, message_buffer(i), md);
       } else {
         const int j = i * K + m - 1;
         const int s = __builtin_amdgcn_readlane(wslot, j);
         if (s < 0) continue;  // masked
-        copy_row_wave<LINE>(
+        copy_row_wave<true>(
             P.recv + ((uint64_t)rs.expert[j] * (uint64_t)P.max_tokens + (uint64_t)s) * md,
             message_buffer(i), md);
       }
@@ -609,28 +609,30 @@ static hipError_t launch_direct(const DispatchParams& p, hipStream_t stream) {
   return launch_direct_block<DT, VEC, 256>(p, stream);
 }
 
-template <int DT, bool LINE, int VEC, bool GROUP_ROWS>
+template <int DT, int VEC, bool GROUP_ROWS>
 static hipError_t launch_dt(const DispatchParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   // whole rounds of kXcds tiles, so that the index mapping covers every tile
   const int rounds = (tiles + kXcds - 1) / kXcds;
   const size_t lds = (size_t)p.tile * p.msg_stride + sizeof(int) * hist_cap_for(p.num_experts);
-  dispatch_kernel<DT, LINE, VEC, GROUP_ROWS>
+  dispatch_kernel<DT, VEC, GROUP_ROWS>
       <<<rounds * kXcds * p.groups, kDispatchBlock, lds, stream>>>(p);
   return hipGetLastError();
 }
 
 template <int DT, bool GROUP_ROWS>
-static hipError_t launch_lines(const DispatchParams& p, hipStream_t stream) {
-  return p.wide_idx ? launch_dt<DT, true, 4, GROUP_ROWS>(p, stream)
-                    : launch_dt<DT, true, 1, GROUP_ROWS>(p, stream);
+static hipError_t launch_lds(const DispatchParams& p, hipStream_t stream) {
+  return p.wide_idx ? launch_dt<DT, 4, GROUP_ROWS>(p, stream)
+                    : launch_dt<DT, 1, GROUP_ROWS>(p, stream);
 }
 
+// Below 64 MiB of rows the register-direct kernel; at 64 MiB or more the
+// LDS kernel with whole-line stores.
 template <int DT>
 static hipError_t launch_modes(const DispatchParams& p, hipStream_t stream) {
   if (!p.line_align)
     return p.wide_idx ? launch_direct<DT, 4>(p, stream) : launch_direct<DT, 1>(p, stream);
-  return p.group_rows ? launch_lines<DT, true>(p, stream) : launch_lines<DT, false>(p, stream);
+  return p.group_rows ? launch_lds<DT, true>(p, stream) : launch_lds<DT, false>(p, stream);
 }
 
 hipError_t launch_dispatch(const DispatchParams& p, int dtype, hipStream_t stream) {
