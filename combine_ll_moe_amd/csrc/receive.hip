@@ -17,11 +17,12 @@
 // loads and scans them in LDS until their sum reaches the expected number,
 // at most max_spins times, and posts the outcome in a status word the
 // caller zeroed (with a second bit when its first look found the set
-// incomplete, so that a caller can tell that the call did overlap); every other workgroup looks at the counts once itself and,
-// if they do not add up yet, polls that one word, then scans the (now
-// final) counts. Each takes a contiguous run of the
-// flattened (expert, slot) rows; each wavefront copies whole rows, so that a row's buffer descriptor
-// is uniform and its payload can be read with device-coherent (sc1) loads.
+// incomplete, so that a caller can tell that the call did overlap); every
+// other workgroup looks at the counts once itself and, if they do not add
+// up yet, polls that one word, then scans the (now final) counts. Each
+// takes a contiguous run of the flattened (expert, slot) rows; each
+// wavefront copies whole rows, so that a row's buffer descriptor is
+// uniform and its payload can be read with device-coherent (sc1) loads.
 // Those loads are served at device scope, like the polls, and issue after
 // the polls have seen the full sum: they cannot return a stale L2 line, and
 // no acquire fence (an L2 invalidate per workgroup) is needed.

@@ -26,15 +26,16 @@
 //    with the header load), next row's loads in flight while the current
 //    row is stored: straight from registers with dword-aligned stores below
 //    64 MiB of staged rows, through LDS with destination-aligned whole-line
-//    stores above (mostly HBM-bound writes). Release as in the dispatch: device-coherent
-//    stores, each wave waits for its own, a barrier, then wave 0 adds per
-//    distinct expert the rows it staged to the flag with one device-scope
-//    atomic on the word's high half.
+//    stores above (mostly HBM-bound writes). Release as in the dispatch:
+//    device-coherent stores, each wave waits for its own, a barrier, then
+//    wave 0 adds per distinct expert the rows it staged to the flag with one
+//    device-scope atomic on the word's high half.
 //  - Token side. Workgroup 0 polls every expert's flag (relaxed
 //    device-scope loads, at most max_spins rounds) and posts the outcome in
 //    a caller-zeroed status word; every other workgroup looks at the flags
 //    once and, if some are down, polls that one word, so that the waiting
-//    adds almost no traffic to the signal words the expert side is raising. Then work items of (tile of tokens, run of columns), as the
+//    adds almost no traffic to the signal words the expert side is raising.
+//    Then work items of (tile of tokens, run of columns), as the
 //    fused combine but with no routing prologue (a token's staging row for
 //    pick k is e * max_tokens + t), over a grid of at most kRecvBlocks
 //    workgroups that leaves a not-yet-started expert side room to run: the
@@ -57,7 +58,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // mapping (mostly HBM-bound writes); smaller ones stay in the caches.
 constexpr uint64_t kSendLineBytes = 64ull << 20;
 
-template <bool LINE>
+// Staging through LDS with destination-aligned whole-line stores, for
+// batches of kSendLineBytes or more (mostly HBM-bound writes).
 __device__ __forceinline__ void stage_rows(const SendParams& P, uint32_t* pre, uint8_t* lds_msg,
                                            uint32_t msg_stride, int nbuf, uint32_t r0, uint32_t r1) {
   constexpr int kStage = 4;
@@ -104,7 +106,7 @@ __device__ __forceinline__ void stage_rows(const SendParams& P, uint32_t* pre, u
       if (i + 1 < n) load_row<kStage>(v, src_row(i + 1), chunks);
       const int e = __builtin_amdgcn_readlane(e_l, i);
       if (t >= 0 && t < P.max_tokens)
-        copy_message<LINE>(P.stage + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)t) * mc, msg, mc);
+        copy_message<true>(P.stage + ((uint64_t)e * (uint64_t)P.max_tokens + (uint64_t)t) * mc, msg, mc);
     }
 
     // release: this wave's stores are complete, then every wave's; wave 0
@@ -214,7 +216,7 @@ __global__ void __launch_bounds__(kSendBlock) combine_send_kernel(const SendPara
   uint8_t* lds_msg = lds_raw + count_prefix_bytes(P.num_experts) + kMsgLdsOffset;
   const uint32_t msg_stride = ((uint32_t)kMsgLdsOffset + P.comb_bytes + 15u) & ~15u;
   if ((uint64_t)rows * P.comb_bytes >= kSendLineBytes)
-    stage_rows<true>(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
+    stage_rows(P, pre, lds_msg, msg_stride, P.nbuf, r0, r1);
   else
     stage_rows_direct(P, pre, r0, r1);
 }
