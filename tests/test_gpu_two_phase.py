@@ -74,8 +74,8 @@ def test_two_phase_ragged(n, dtype):
     (40, 48, 64, 1000, 4, W.BF16),    # count prefix in 4 rounds
     (40, 40, 64, 4096, 4, W.BF16),    # largest expert count: 16 rounds
     (24, 24, 256, 300, 12, W.FP8_E4M3),
-    (6, 6, 22520, 4, 2, W.BF16),      # largest message: one LDS buffer, rows past 4 rounds
-    (9, 9, 10240, 3, 2, W.FP8_E4M3),  # two LDS buffers, rows past 4 rounds
+    (6, 6, 22520, 4, 2, W.BF16),      # largest message, rows from registers past one round
+    (9, 9, 10240, 3, 2, W.FP8_E4M3),  # rows from registers past one round
 ])
 @pytest.mark.parametrize("pad", [0, 16, 48])
 def test_two_phase_shapes_and_phases(shape, pad):
@@ -85,6 +85,22 @@ def test_two_phase_shapes_and_phases(shape, pad):
     st = Step(w, full_image=True, base_pad=pad)
     for q in (0, 1):
         _two_phase_step(st, q, x, idx, wt, y)
+
+
+@pytest.mark.parametrize("pad", [0, 16])
+def test_two_phase_staging_through_lds(pad):
+    """64 MiB of staged rows or more go through LDS with whole-line stores:
+    2048 rows of the largest message (one LDS buffer, rows past four
+    rounds)."""
+    w = W.Workload("lds_stage", 1024, 22520, 16, 2, W.BF16, "uniform", max_tokens=1024, seed=31)
+    mc = 4 + 2 * w.hidden
+    assert w.num_tokens * w.topk * mc >= 64 << 20
+    x, idx, wt = W.tokens(w), W.routing(w), W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    st = Step(w, full_image=False, base_pad=pad)
+    for q in (0, 1):
+        _two_phase_step(st, q, x, idx, wt, y)
+        say(f"[two-phase] staging through LDS, pad {pad}, parity {q} ok")
 
 
 def test_two_phase_many_rows_per_workgroup():
