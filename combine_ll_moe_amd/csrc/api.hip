@@ -132,7 +132,6 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   p.groups = groups < 1 ? 1 : groups;
   p.group_rows = dtype == kBf16 && p.groups > 1;
   p.tile = tile_for(num_tokens, p.groups, topk, kDispatchTileBlocks);
-  p.block = kDispatchBlock;
   p.msg_bytes = (uint32_t)L.dispatch_msg;
   p.msg_stride = ((uint32_t)kMsgLdsOffset + p.msg_bytes + 15u) & ~15u;
   // every message of a tile sits in LDS at once

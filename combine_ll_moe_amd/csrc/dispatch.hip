@@ -604,9 +604,7 @@ static hipError_t launch_direct_block(const DispatchParams& p, hipStream_t strea
 
 template <int DT, int VEC>
 static hipError_t launch_direct(const DispatchParams& p, hipStream_t stream) {
-  if (p.block == 1024) return launch_direct_block<DT, VEC, 1024>(p, stream);
-  if (p.block == 512) return launch_direct_block<DT, VEC, 512>(p, stream);
-  return launch_direct_block<DT, VEC, 256>(p, stream);
+  return launch_direct_block<DT, VEC, kDispatchBlock>(p, stream);
 }
 
 template <int DT, int VEC, bool GROUP_ROWS>

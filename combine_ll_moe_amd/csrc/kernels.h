@@ -25,7 +25,6 @@ struct DispatchParams {
   uint32_t msg_bytes;              // md
   uint32_t msg_stride;             // LDS path: bytes of one message buffer (one per tile token)
   int line_align;                  // 64 MiB of rows or more: the LDS path, whole-line stores
-  int block;                       // threads per workgroup of the register-direct dispatch
   int wide_idx;                    // routing prologue reads 4 entries per load
 };
 
