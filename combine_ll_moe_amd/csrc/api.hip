@@ -179,13 +179,14 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   p.hidden = hidden;
   p.num_experts = num_experts;
   p.topk = topk;
-  const CombineShape shape = combine_shape(num_tokens, hidden, topk);
-  p.slices = shape.slices;
-  p.tile = shape.tile;
   // Large gathers stream past the caches: read with non-temporal loads they
   // leave L2 and MALL to the next dispatch's traffic (a whole step is ~20%
   // faster at 117 MB of rows); small ones gain from the cached path.
   p.stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
+  const CombineShape shape = combine_shape(num_tokens, hidden, topk, p.stream_rows);
+  p.slices = shape.slices;
+  p.tile = shape.tile;
+  p.block = shape.block;
   return from_hip(launch_combine(p, stream));
 }
 
@@ -280,11 +281,13 @@ extern "C" int ll_moe_combine_recv(void* layout, int max_tokens, int num_tokens,
   p.hidden = hidden;
   p.num_experts = num_experts;
   p.topk = topk;
-  p.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
-  p.tile = tile_for(num_tokens, p.slices, topk);
   p.comb_bytes = (uint32_t)L.combine_msg;
   p.max_spins = max_spins;
   p.stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
+  const CombineShape shape = combine_shape(num_tokens, hidden, topk, p.stream_rows);
+  p.slices = shape.slices;
+  p.tile = shape.tile;
+  p.block = shape.block;
   return from_hip(launch_combine_recv(p, stream));
 }
 

@@ -11,7 +11,7 @@
 // expert outputs, as a one-shot reduction replaces push-then-fold.
 //
 // Design on gfx950: one workgroup per (tile of consecutive tokens, run of
-// columns). It computes the tile's slots once (route.h); then, token by
+// columns); the runs of a row are equal, one 16-byte chunk per thread. It computes the tile's slots once (route.h); then, token by
 // token, every thread issues its topk 16-byte loads of bf16 expert rows at
 // once (all outstanding together), folds them with v_fma_f32 in k order,
 // and writes 8 fp32 results as two 16-byte streaming stores (gather.h).
@@ -49,12 +49,12 @@ __device__ __forceinline__ void combine_token(const CombineParams& P, const Rout
 }
 
 template <int MAXK, bool STREAM>
-__global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombineParams P) {
+__global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const CombineParams P) {
   __shared__ RouteShared rs;
   extern __shared__ int hist[];  // hist_cap_for(num_experts) ints
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
-    for (int e = tid; e < P.num_experts; e += kCombineBlock) P.sig_other[e] = 0;
+    for (int e = tid; e < P.num_experts; e += (int)blockDim.x) P.sig_other[e] = 0;
 
   // workgroup -> (tile of tokens [t0, t1), run of columns sl)
   const int tile = blockIdx.x / P.slices;
@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kCombineBlock) combine_kernel(const CombinePar
              hist_cap_for(P.num_experts));
 
   const int chunks = P.hidden / 8;
-  const int c = sl * kCombineBlock + tid;
+  const int c = sl * (int)blockDim.x + tid;
   if (c >= chunks) return;
   for (int t = t0; t < t1; ++t) combine_token<MAXK, STREAM>(P, rs, t, t - t0, c, chunks);
 }
@@ -80,13 +80,13 @@ template <bool STREAM>
 static void launch_k(const CombineParams& p, int blocks, hipStream_t stream) {
   const size_t lds = sizeof(int) * hist_cap_for(p.num_experts);
   if (p.topk <= 2)
-    combine_kernel<2, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
+    combine_kernel<2, STREAM><<<blocks, p.block, lds, stream>>>(p);
   else if (p.topk <= 4)
-    combine_kernel<4, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
+    combine_kernel<4, STREAM><<<blocks, p.block, lds, stream>>>(p);
   else if (p.topk <= 8)
-    combine_kernel<8, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
+    combine_kernel<8, STREAM><<<blocks, p.block, lds, stream>>>(p);
   else
-    combine_kernel<16, STREAM><<<blocks, kCombineBlock, lds, stream>>>(p);
+    combine_kernel<16, STREAM><<<blocks, p.block, lds, stream>>>(p);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {

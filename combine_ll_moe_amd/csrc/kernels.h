@@ -41,6 +41,7 @@ struct CombineParams {
   int topk;
   int tile;                        // consecutive tokens per workgroup
   int slices;                      // workgroups per tile, each a contiguous run of columns
+  int block;                       // threads per workgroup (one 16-byte column chunk each)
   int stream_rows;                 // read the expert rows with non-temporal loads
 };
 
@@ -73,6 +74,7 @@ struct RecvParams {                // two-phase combine, token side
   int topk;
   int tile;                        // consecutive tokens per workgroup
   int slices;                      // workgroups per tile, each a contiguous run of columns
+  int block;                       // threads per workgroup (one 16-byte column chunk each)
   uint32_t comb_bytes;             // mc
   int max_spins;                   // polls of one flag before its wait gives up
   int stream_rows;                 // read the staging rows with non-temporal loads
@@ -128,7 +130,11 @@ constexpr int kCachePolicySc1 = 16;
 constexpr int kCachePolicyNt = 2;  // non-temporal (streaming)
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
+// Combine workgroups: at most kCombineBlock threads (kCombineWideBlock for
+// gathers of kStreamRowsBytes or more), kCombineMaxBlock in any case.
 constexpr int kCombineBlock = 256;
+constexpr int kCombineWideBlock = 448;
+constexpr int kCombineMaxBlock = 512;
 
 // Launch shapes shared by the combine and the gather probe. A workgroup
 // takes a tile of consecutive tokens and one run of columns; tiles grow
@@ -147,17 +153,29 @@ inline int tile_for(int num_tokens, int per_token_blocks, int topk, int target =
   if (tile > kTileEntryLimit / topk) tile = kTileEntryLimit / topk;
   return tile < 1 ? 1 : tile;
 }
-// The combine's launch shape: a workgroup of kCombineBlock threads (8
-// columns each) takes a tile of `tile` tokens and a run of 2048 columns;
-// `slices` runs cover a row. (Workgroups covering a whole row, so that a
-// tile's routing prologue ran once per tile, measured slower: 1024 tokens
-// of 7168 columns 30.3 against 29.8 us.)
+// The combine's launch shape: a workgroup of `block` threads (8 columns
+// each) takes a tile of `tile` tokens and one of `slices` equal runs of
+// columns that cover a row. Equal runs measured faster than runs of 256
+// threads with a short last one (a 7168-column row in runs of 256, 256,
+// 256 and 128 threads: 128 tokens 5.13 us, 1024 tokens 29.8; in four runs
+// of 224: 5.04 and 29.1), although the gather alone, rows handed in,
+// takes the same time in both shapes (1024 tokens: 27.9 us), and dealing
+// the short runs evenly to the XCDs made the combine slower (5.95, 30.0).
+// Large gathers take longer runs, fewer workgroups and so fewer routing
+// prologues: two runs of 448 threads, 1024 tokens of 7168 columns in 29.0
+// us. A block is a multiple of 32 threads and at least one wavefront (the
+// routing prologue holds a tile's entries in wavefront 0's lanes).
 struct CombineShape {
-  int slices, tile;
+  int slices, tile, block;
 };
-inline CombineShape combine_shape(int num_tokens, int hidden, int topk) {
+inline CombineShape combine_shape(int num_tokens, int hidden, int topk, bool stream_rows) {
   CombineShape s;
-  s.slices = (hidden / 8 + kCombineBlock - 1) / kCombineBlock;
+  const int chunks = hidden / 8;
+  const int most = stream_rows ? kCombineWideBlock : kCombineBlock;
+  s.slices = (chunks + most - 1) / most;
+  const int even = (chunks + s.slices - 1) / s.slices;
+  s.block = (even + 31) / 32 * 32;
+  if (s.block < 64) s.block = 64;
   s.tile = tile_for(num_tokens, s.slices, topk);
   return s;
 }

@@ -203,14 +203,14 @@ hipError_t launch_store_rows_policy(int policy, uint8_t* base, const int64_t* of
 // run of columns), each token's picks folded by gather_fold. A row outside
 // [0, y_rows) (a masked pick is -1) takes no part.
 template <int MAXK, bool STREAM>
-__global__ void __launch_bounds__(kCombineBlock)
+__global__ void __launch_bounds__(kCombineMaxBlock)
     gather_rows_kernel(const g32x4* __restrict__ y, int64_t y_rows, const int32_t* __restrict__ rows,
                        const float* __restrict__ wt, gf32x4* __restrict__ out, int num_tokens,
                        int topk, int chunks, int tile, int slices) {
   const int tl = blockIdx.x / slices;
   const int sl = blockIdx.x - tl * slices;
   const int t0 = tl * tile;
-  const int c = sl * kCombineBlock + threadIdx.x;
+  const int c = sl * (int)blockDim.x + threadIdx.x;
   if (t0 >= num_tokens || c >= chunks) return;
   const int t1 = t0 + tile < num_tokens ? t0 + tile : num_tokens;
   for (int t = t0; t < t1; ++t) {
@@ -233,9 +233,9 @@ __global__ void __launch_bounds__(kCombineBlock)
 template <bool STREAM>
 void launch_gather_rows_k(int blocks, const g32x4* y, int64_t y_rows, const int32_t* rows,
                           const float* wt, gf32x4* out, int num_tokens, int topk, int chunks,
-                          int tile, int slices, hipStream_t stream) {
+                          int tile, int slices, int block, hipStream_t stream) {
 #define LLMOE_GATHER(K)                                                                      \
-  gather_rows_kernel<K, STREAM><<<blocks, kCombineBlock, 0, stream>>>(                       \
+  gather_rows_kernel<K, STREAM><<<blocks, block, 0, stream>>>(                               \
       y, y_rows, rows, wt, out, num_tokens, topk, chunks, tile, slices)
   if (topk <= 2)
     LLMOE_GATHER(2);
@@ -322,16 +322,16 @@ extern "C" int ll_moe_diag_gather_rows(const void* y, long long y_rows, int hidd
     return LL_MOE_INVALID_ARGUMENT;
   if ((int64_t)num_tokens * topk > INT32_MAX) return LL_MOE_INVALID_ARGUMENT;
   const int chunks = hidden / 8;
-  const CombineShape shape = combine_shape(num_tokens, hidden, topk);
-  const int blocks = ((num_tokens + shape.tile - 1) / shape.tile) * shape.slices;
   const bool stream_rows = (uint64_t)num_tokens * topk * hidden * 2 >= kStreamRowsBytes;
+  const CombineShape shape = combine_shape(num_tokens, hidden, topk, stream_rows);
+  const int blocks = ((num_tokens + shape.tile - 1) / shape.tile) * shape.slices;
   const g32x4* yy = static_cast<const g32x4*>(y);
   gf32x4* o = reinterpret_cast<gf32x4*>(out);
   if (stream_rows)
     launch_gather_rows_k<true>(blocks, yy, y_rows, rows, weights, o, num_tokens, topk, chunks,
-                               shape.tile, shape.slices, stream);
+                               shape.tile, shape.slices, shape.block, stream);
   else
     launch_gather_rows_k<false>(blocks, yy, y_rows, rows, weights, o, num_tokens, topk, chunks,
-                                shape.tile, shape.slices, stream);
+                                shape.tile, shape.slices, shape.block, stream);
   return from_hip(hipGetLastError());
 }

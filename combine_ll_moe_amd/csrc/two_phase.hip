@@ -293,7 +293,7 @@ __device__ __forceinline__ void fold_token(const RecvParams& P, int t, int c, in
 }
 
 template <int MAXK, bool STREAM>
-__global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvParams P) {
+__global__ void __launch_bounds__(kCombineMaxBlock) combine_recv_kernel(const RecvParams P) {
   const int tid = threadIdx.x;
   const int E = P.num_experts;
   if (blockIdx.x == 0)
@@ -394,13 +394,13 @@ __global__ void __launch_bounds__(kCombineBlock) combine_recv_kernel(const RecvP
 template <bool STREAM>
 static void launch_recv_k(const RecvParams& p, int blocks, hipStream_t stream) {
   if (p.topk <= 2)
-    combine_recv_kernel<2, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_recv_kernel<2, STREAM><<<blocks, p.block, 0, stream>>>(p);
   else if (p.topk <= 4)
-    combine_recv_kernel<4, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_recv_kernel<4, STREAM><<<blocks, p.block, 0, stream>>>(p);
   else if (p.topk <= 8)
-    combine_recv_kernel<8, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_recv_kernel<8, STREAM><<<blocks, p.block, 0, stream>>>(p);
   else
-    combine_recv_kernel<16, STREAM><<<blocks, kCombineBlock, 0, stream>>>(p);
+    combine_recv_kernel<16, STREAM><<<blocks, p.block, 0, stream>>>(p);
 }
 
 hipError_t launch_combine_recv(const RecvParams& p, hipStream_t stream) {

@@ -127,6 +127,24 @@ def test_large_dispatch_whole_line_stores(shape):
         _run_step(st, q, x, idx, wt, y)
 
 
+@pytest.mark.parametrize("shape", [
+    # (N, h, E, K, dtype, routing): the combine splits a row into equal runs
+    # of columns, one 16-byte chunk per thread, blocks a multiple of 32
+    (128, 1032, 16, 4, W.BF16, "uniform"),      # 129 chunks: one run of 160 threads
+    (96, 7168, 32, 8, W.FP8_E4M3, "uniform"),   # four runs of 224 (a half wavefront each)
+    (128, 2056, 16, 8, W.BF16, "uniform"),      # 257 chunks: two runs of 160, the last 97
+    (1024, 4104, 64, 8, W.BF16, "hotset"),      # streamed rows: two runs of 288, the last 225
+])
+def test_combine_column_runs(shape):
+    n, h, e, k, dt, routing = shape
+    w = W.Workload("runs", n, h, e, k, dt, routing, seed=h + k)
+    say(f"[parity] combine column runs: N={n} h={h} E={e} K={k} dtype={dt}")
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    for q in (0, 1):
+        _run_step(st, q, x, idx, wt, y)
+
+
 def test_masked_repeated_and_overflowing_picks():
     w = W.Workload("mask", 6, 64, 4, 3, W.BF16, "uniform", max_tokens=6, seed=9)
     x = W.tokens(w)

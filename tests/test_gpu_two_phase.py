@@ -87,6 +87,24 @@ def test_two_phase_shapes_and_phases(shape, pad):
         _two_phase_step(st, q, x, idx, wt, y)
 
 
+@pytest.mark.parametrize("shape", [
+    # (N, h, E, K): the token side's equal runs of columns, as the fused
+    # combine's: one run of 160 threads (129 chunks; the last wavefront half
+    # there), two of 160, and two streamed runs of 288
+    (128, 1032, 16, 4),
+    (128, 2056, 16, 8),
+    (1024, 4104, 64, 8),
+])
+def test_two_phase_column_runs(shape):
+    n, h, e, k = shape
+    w = W.Workload("runs", n, h, e, k, W.BF16, "hotset", seed=h + n)
+    say(f"[two-phase] column runs: N={n} h={h} E={e} K={k}")
+    x, idx, wt, y = _inputs(w)
+    st = Step(w, full_image=False)
+    for q in (0, 1):
+        _two_phase_step(st, q, x, idx, wt, y)
+
+
 @pytest.mark.parametrize("pad", [0, 16])
 def test_two_phase_staging_through_lds(pad):
     """64 MiB of staged rows or more go through LDS with whole-line stores:
