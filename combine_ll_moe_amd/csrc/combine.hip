@@ -11,11 +11,12 @@
 // expert outputs, as a one-shot reduction replaces push-then-fold.
 //
 // Design on gfx950: one workgroup per (tile of consecutive tokens, run of
-// columns); the runs of a row are equal, one 16-byte chunk per thread. It computes the tile's slots once (route.h); then, token by
-// token, every thread issues its topk 16-byte loads of bf16 expert rows at
-// once (all outstanding together), folds them with v_fma_f32 in k order,
-// and writes 8 fp32 results as two 16-byte streaming stores (gather.h).
-// Workgroup 0 zeroes the other set's signal words.
+// columns); the runs of a row are equal, one 16-byte chunk per thread
+// (kernels.h, combine_shape). It computes the tile's slots once (route.h);
+// then, token by token, every thread issues its topk 16-byte loads of bf16
+// expert rows at once (all outstanding together), folds them with
+// v_fma_f32 in k order, and writes 8 fp32 results as two 16-byte streaming
+// stores (gather.h). Workgroup 0 zeroes the other set's signal words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
