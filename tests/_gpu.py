@@ -213,3 +213,31 @@ def check_combine(out: np.ndarray, ref: np.ndarray, rel: float = 1e-6):
         assert np.isfinite(out).all()
         assert err.max() <= rel, f"max rel err {err.max()}"
     return int((out.view(np.uint32) != ref.view(np.uint32)).sum())
+
+
+def random_case(rng):
+    """A seeded random shape and routing: any dtype, hidden, expert count,
+    top-k, batch and capacity the ABI accepts (layouts up to ~256 MiB), with
+    repeated experts, masked entries and capacity overflow."""
+    while True:
+        dt = W.FP8_E4M3 if rng.random() < 0.4 else W.BF16
+        kind = rng.random()
+        if kind < 0.2:    # long batches: tiles of two tokens
+            n = int(rng.integers(1025, 2100))
+            h = 128 * int(rng.integers(1, 4))
+            e = int(rng.integers(1, 65))
+        else:
+            n = int(rng.integers(0, 700))
+            h = 128 * int(rng.integers(1, 80)) if dt == W.FP8_E4M3 else 8 * int(rng.integers(1, 1600))
+            # few experts in some cases: picks repeat and overflow the capacity
+            e = int(rng.integers(1, 5)) if kind < 0.35 else int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(e, ll.MAX_TOPK) + 1))
+        cap = max(1, n + (0 if kind < 0.35 else int(rng.integers(0, 40))))
+        md, mc = oracle.message_bytes(h, dt)
+        if n <= cap and md <= ll.MAX_MESSAGE_BYTES and e * cap * max(md, mc) <= 1 << 26:
+            break
+    idx = rng.integers(0, e, (n, k)).astype(np.int32)  # repeats allowed
+    mask = rng.random((n, k)) < 0.03
+    idx[mask] = np.where(rng.random(int(mask.sum())) < 0.5, -1, e + 3).astype(np.int32)
+    return W.Workload("random", n, h, e, k, dt, "uniform", max_tokens=cap,
+                      seed=int(rng.integers(1 << 30))), idx

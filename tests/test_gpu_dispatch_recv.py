@@ -16,7 +16,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines t
 import combine_ll_moe_amd as ll  # noqa: E402
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from _gpu import DEV, Step, say, to_dev  # noqa: E402
+from _gpu import DEV, Step, random_case, say, to_dev  # noqa: E402
 
 SENT = 0xA5
 FULL_COMPARE_BYTES = 256 << 20
@@ -273,3 +273,29 @@ def test_unpack_graph_replays(name):
             if ref[1] is not None:
                 assert torch.equal(o.scales.view(torch.int32), ref[1].view(torch.int32))
         say(f"[unpack graph] {name} replay {r} ok")
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_unpack_random_shapes(block):
+    """20 seeded random cases (10 per block; any dtype, hidden, expert count,
+    top-k, batch and capacity, with repeats, masks and overflow) through the
+    dispatch and the expert side, both parities, each against the oracle;
+    every layout at a random 16-byte phase of its allocation."""
+    for case in range(10):
+        rng = np.random.default_rng(4000 + 10 * block + case)
+        w, idx = random_case(rng)
+        pad = int(rng.choice([0, 16, 32, 48]))
+        _, cnt = oracle.route(idx, w.num_experts, w.capacity)
+        expected = int(cnt.sum())  # routed messages: masked and overflowing picks excluded
+        say(f"[unpack] random case {10 * block + case}: N={w.num_tokens} cap={w.capacity} "
+            f"h={w.hidden} E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad} "
+            f"messages={expected}")
+        x = W.tokens(w)
+        st = Step(w, full_image=False, base_pad=pad)
+        for q in (0, 1):
+            outs = Outputs(w)
+            st.dispatch(q, x, idx)
+            outs.launch(st, q, expected)
+            _check(st, q, outs, expected, _filled(w, idx))
+        del st
+        torch.cuda.empty_cache()

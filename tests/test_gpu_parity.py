@@ -14,7 +14,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines t
 import combine_ll_moe_amd as ll  # noqa: E402
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from _gpu import DEV, Step, check_combine, filled_mask, say, to_dev  # noqa: E402
+from _gpu import DEV, Step, check_combine, filled_mask, random_case, say, to_dev  # noqa: E402
 
 
 def _inputs(w: W.Workload, dense_y=False):
@@ -457,34 +457,6 @@ def test_repeated_calls_same_bits():
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
-def _random_case(rng):
-    """A seeded random shape and routing: any dtype, hidden, expert count,
-    top-k, batch and capacity the ABI accepts (layouts up to ~256 MiB), with
-    repeated experts, masked entries and capacity overflow."""
-    while True:
-        dt = W.FP8_E4M3 if rng.random() < 0.4 else W.BF16
-        kind = rng.random()
-        if kind < 0.2:    # long batches: tiles of two tokens
-            n = int(rng.integers(1025, 2100))
-            h = 128 * int(rng.integers(1, 4))
-            e = int(rng.integers(1, 65))
-        else:
-            n = int(rng.integers(0, 700))
-            h = 128 * int(rng.integers(1, 80)) if dt == W.FP8_E4M3 else 8 * int(rng.integers(1, 1600))
-            # few experts in some cases: picks repeat and overflow the capacity
-            e = int(rng.integers(1, 5)) if kind < 0.35 else int(rng.integers(1, 300))
-        k = int(rng.integers(1, min(e, ll.MAX_TOPK) + 1))
-        cap = max(1, n + (0 if kind < 0.35 else int(rng.integers(0, 40))))
-        md, mc = oracle.message_bytes(h, dt)
-        if n <= cap and md <= ll.MAX_MESSAGE_BYTES and e * cap * max(md, mc) <= 1 << 26:
-            break
-    idx = rng.integers(0, e, (n, k)).astype(np.int32)  # repeats allowed
-    mask = rng.random((n, k)) < 0.03
-    idx[mask] = np.where(rng.random(int(mask.sum())) < 0.5, -1, e + 3).astype(np.int32)
-    return W.Workload("random", n, h, e, k, dt, "uniform", max_tokens=cap,
-                      seed=int(rng.integers(1 << 30))), idx
-
-
 @pytest.mark.parametrize("block", range(4))
 def test_random_shapes(block):
     """40 seeded random cases (10 per block) through dispatch and combine,
@@ -492,7 +464,7 @@ def test_random_shapes(block):
     16-byte phase of its allocation."""
     for case in range(10):
         rng = np.random.default_rng(1000 + 10 * block + case)
-        w, idx = _random_case(rng)
+        w, idx = random_case(rng)
         pad = int(rng.choice([0, 16, 32, 48]))
         say(f"[parity] random case {10 * block + case}: N={w.num_tokens} cap={w.capacity} "
             f"h={w.hidden} E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad}")

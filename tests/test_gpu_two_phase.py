@@ -15,7 +15,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines t
 import combine_ll_moe_amd as ll  # noqa: E402
 import oracle  # noqa: E402
 import workloads as W  # noqa: E402
-from _gpu import DEV, Step, check_combine, filled_mask, say, to_dev  # noqa: E402
+from _gpu import DEV, Step, check_combine, filled_mask, random_case, say, to_dev  # noqa: E402
 
 # a hold of about 0.5 ms on the expert side's stream, so that the token side
 # is already waiting when the staging starts
@@ -316,3 +316,32 @@ def test_two_phase_masked_entries():
     for q in (0, 1):
         out = _two_phase_step(st, q, x, idx, wt, y)
         assert (out[41].view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("block", range(2))
+def test_two_phase_random_shapes(block):
+    """20 seeded random cases (10 per block; any dtype, hidden, expert count,
+    top-k, batch and capacity, with masks and overflow) through the dispatch
+    and the two-phase combine, both parities, each against the oracle; every
+    layout at a random 16-byte phase of its allocation. The two-phase
+    combine takes at most one pick per (token, expert): a repeated expert
+    is masked here."""
+    for case in range(10):
+        rng = np.random.default_rng(3000 + 10 * block + case)
+        w, idx = random_case(rng)
+        for t in range(idx.shape[0]):
+            _, first = np.unique(idx[t], return_index=True)
+            again = np.ones(idx.shape[1], bool)
+            again[first] = False
+            idx[t, again] = -1
+        pad = int(rng.choice([0, 16, 32, 48]))
+        say(f"[two-phase] random case {10 * block + case}: N={w.num_tokens} cap={w.capacity} "
+            f"h={w.hidden} E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad}")
+        x, wt = W.tokens(w), W.weights(w)
+        y = W.expert_outputs(w, filled_mask(w, idx))
+        st = Step(w, full_image=False, base_pad=pad)
+        y_dev = to_dev(y)
+        for q in (0, 1):
+            _two_phase_step(st, q, x, idx, wt, y, y_dev)
+        del st, y_dev
+        torch.cuda.empty_cache()
