@@ -39,8 +39,13 @@ namespace llmoe {
 // KROUND: 16-byte loads in flight per lane before their stores (16 for
 // the bandwidth-bound copies of 64 MiB or more: 1024 tokens of 7168
 // columns 44.6 against 44.8 us with 8; 8 below, where 16 measured slower,
-// 6.9 against 6.6 us at 128 tokens).
-template <int KROUND>
+// 6.9 against 6.6 us at 128 tokens). STREAM_OUT: the payload rows go out
+// with non-temporal stores, so that they do not evict from the MALL the
+// receive rows still to be read (for 64 MiB or more: 1024 tokens of 7168
+// columns unpacked in 39.0 against 45.1 us, and a dispatch followed by its
+// unpack in 67.5 against 76.8; at 128 tokens plain stores keep the
+// dispatch-and-unpack step shorter, 15.3 against 15.9 us).
+template <int KROUND, bool STREAM_OUT>
 __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   __shared__ uint32_t wave_sum[kSendBlock / kWave];
@@ -140,7 +145,12 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
 #pragma unroll
         for (int u = 0; u < kRound; ++u) {
           const uint32_t c = c0 + u * kWave;
-          if (c < nch) dst[c] = v[u];
+          if (c < nch) {
+            if constexpr (STREAM_OUT)
+              __builtin_nontemporal_store(v[u], dst + c);
+            else
+              dst[c] = v[u];
+          }
         }
       }
       for (uint32_t s = lane; s < nsc; s += kWave)
@@ -152,9 +162,11 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
 
 hipError_t launch_dispatch_recv(const UnpackParams& p, int blocks, hipStream_t stream) {
   if (p.wide)
-    dispatch_recv_kernel<16><<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
+    dispatch_recv_kernel<16, true>
+        <<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
   else
-    dispatch_recv_kernel<8><<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
+    dispatch_recv_kernel<8, false>
+        <<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
   return hipGetLastError();
 }
 
