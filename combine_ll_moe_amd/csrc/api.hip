@@ -295,10 +295,10 @@ namespace {
 // Expert side of the dispatch: a fixed grid, one workgroup per CU, so that
 // while it waits beside a running dispatch it leaves the dispatch room; two
 // per CU when the step routes 64 MiB of messages or more, whose copy is
-// bandwidth-bound (1024 tokens of 7168 columns: unpack 44.6 against 48.7
-// us, and the dispatch with a receiver waiting beside it 81.3 against 86.3
-// us to the expert inputs; four per CU unpack no faster and slow that
-// dispatch to 86.9).
+// bandwidth-bound (1024 tokens of 7168 columns, measured with plain
+// payload stores: unpack 44.6 against 48.7 us, and the dispatch with a
+// receiver waiting beside it 81.3 against 86.3 us to the expert inputs;
+// four per CU unpack no faster and slow that dispatch to 86.9).
 constexpr int kUnpackBlocks = 256;
 constexpr int kUnpackWideBlocks = 512;
 }  // namespace
