@@ -9,7 +9,11 @@
  *   abi_consumer gpu    dispatch and combine of a small seeded batch, both
  *                       parities, bf16 and fp8 payloads, on the GPU; the
  *                       whole layout byte for byte and the combine output
- *                       bit for bit against the oracle
+ *                       bit for bit against the oracle; then, on routings
+ *                       with distinct experts per token, the expert side
+ *                       (ll_moe_dispatch_recv: payload, scales, sources and
+ *                       counts byte for byte) and the two-phase combine
+ *                       (ll_moe_combine_send / _recv: layout and output)
  * Prints "ok" and exits 0 on success; prints the first mismatch and exits 1
  * otherwise.
  */
@@ -31,6 +35,16 @@ int oracle_combine(uint8_t* image, int max_tokens, int num_tokens, int hidden,
                    float* out);
 int oracle_clean(uint8_t* image, int max_tokens, int hidden, int num_experts, int dtype,
                  int parity);
+int oracle_route(int num_tokens, int topk, int num_experts, int max_tokens, const int32_t* idx,
+                 int32_t* slot, int64_t* cnt);
+int oracle_combine_send(uint8_t* image, int max_tokens, int hidden, int num_experts, int dtype,
+                        int parity, const uint16_t* expert_out);
+int oracle_combine_recv(uint8_t* image, int max_tokens, int num_tokens, int hidden,
+                        int num_experts, int topk, int dtype, int parity, const int32_t* idx,
+                        const float* weights, float* out);
+int oracle_dispatch_recv(uint8_t* image, int max_tokens, int hidden, int num_experts, int dtype,
+                         int parity, int expected, uint8_t* payload, float* scales, int32_t* src,
+                         int32_t* counts);
 
 static int fail(const char* what) {
   printf("FAIL: %s\n", what);
@@ -151,6 +165,90 @@ static int gpu_checks(int dtype) {
         return 1;
       }
     if (memcmp(out, ref, (size_t)N * H * 4) != 0) return fail("combine bits differ");
+  }
+  /* the expert side and the two-phase combine: at most one pick per
+   * (token, expert), some picks masked */
+  for (int t = 0; t < N; ++t) {
+    const int first = (int)(lcg() % E);
+    for (int k = 0; k < K; ++k)
+      idx[t * K + k] = (lcg() & 15) == 0 ? -1 : (first + 2 * k) % E;
+  }
+  HIPCHECK(hipMemcpy(d_idx, idx, (size_t)N * K * 4, hipMemcpyHostToDevice));
+  {
+    int32_t slot[N * K];
+    int64_t cnt[E];
+    if (oracle_route(N, K, E, CAP, idx, slot, cnt) != 0) return fail("oracle route");
+    int expected = 0;
+    for (int e = 0; e < E; ++e) expected += (int)cnt[e];
+    const size_t rows = (size_t)E * CAP;
+    const size_t pb = dtype == LL_MOE_BF16 ? 2 * (size_t)H : (size_t)H;
+    const size_t ns = dtype == LL_MOE_BF16 ? 1 : (size_t)H / 128;
+    uint8_t* pay = malloc(rows * pb);
+    uint8_t* pay_ref = malloc(rows * pb);
+    float* sc = malloc(rows * ns * 4);
+    float* sc_ref = malloc(rows * ns * 4);
+    int32_t* src = malloc(rows * 4);
+    int32_t* src_ref = malloc(rows * 4);
+    int32_t counts[E], counts_ref[E], status = 0;
+    if (!pay || !pay_ref || !sc || !sc_ref || !src || !src_ref) return fail("host memory");
+    void *d_pay, *d_sc, *d_src, *d_cnt, *d_status;
+    HIPCHECK(hipMalloc(&d_pay, rows * pb));
+    HIPCHECK(hipMalloc(&d_sc, rows * ns * 4));
+    HIPCHECK(hipMalloc(&d_src, rows * 4));
+    HIPCHECK(hipMalloc(&d_cnt, E * 4));
+    HIPCHECK(hipMalloc(&d_status, 4));
+    for (int q = 0; q < 2; ++q) {
+      /* outputs start as the same sentinel on both sides */
+      memset(pay_ref, 0x5A, rows * pb);
+      memset(sc_ref, 0x5A, rows * ns * 4);
+      memset(src_ref, 0x5A, rows * 4);
+      HIPCHECK(hipMemset(d_pay, 0x5A, rows * pb));
+      HIPCHECK(hipMemset(d_sc, 0x5A, rows * ns * 4));
+      HIPCHECK(hipMemset(d_src, 0x5A, rows * 4));
+      HIPCHECK(hipMemset(d_status, 0, 4));
+      if (ll_moe_dispatch(d_lay, CAP, N, H, E, K, dtype, q, d_x, d_idx, NULL) != LL_MOE_SUCCESS)
+        return fail("dispatch (two-phase)");
+      if (ll_moe_dispatch_recv(d_lay, CAP, H, E, dtype, q, expected, d_pay,
+                               dtype == LL_MOE_BF16 ? NULL : (float*)d_sc, (int32_t*)d_src,
+                               (int32_t*)d_cnt, 1 << 20, (int32_t*)d_status,
+                               NULL) != LL_MOE_SUCCESS)
+        return fail("dispatch_recv");
+      if (ll_moe_combine_send(d_lay, CAP, H, E, dtype, q, d_y, NULL) != LL_MOE_SUCCESS)
+        return fail("combine_send");
+      HIPCHECK(hipDeviceSynchronize());
+      HIPCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+      if ((status & ~LL_MOE_RECV_WAITED) != LL_MOE_RECV_READY) return fail("dispatch_recv status");
+      HIPCHECK(hipMemset(d_status, 0, 4));
+      if (ll_moe_combine_recv(d_lay, CAP, N, H, E, K, dtype, q, d_idx, d_w, d_out, 1 << 20,
+                              (int32_t*)d_status, NULL) != LL_MOE_SUCCESS)
+        return fail("combine_recv");
+      HIPCHECK(hipDeviceSynchronize());
+      HIPCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+      if ((status & ~LL_MOE_RECV_WAITED) != LL_MOE_RECV_READY) return fail("combine_recv status");
+
+      if (oracle_dispatch(image, CAP, N, H, E, K, dtype, q, x, idx) != 0) return fail("oracle");
+      if (oracle_dispatch_recv(image, CAP, H, E, dtype, q, expected, pay_ref,
+                               dtype == LL_MOE_BF16 ? NULL : sc_ref, src_ref, counts_ref) != 0)
+        return fail("oracle dispatch_recv");
+      if (oracle_combine_send(image, CAP, H, E, dtype, q, y) != 0) return fail("oracle send");
+      if (oracle_combine_recv(image, CAP, N, H, E, K, dtype, q, idx, w, ref) != 0)
+        return fail("oracle recv");
+      HIPCHECK(hipMemcpy(pay, d_pay, rows * pb, hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(sc, d_sc, rows * ns * 4, hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(src, d_src, rows * 4, hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(counts, d_cnt, E * 4, hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(got, d_lay, total, hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(out, d_out, (size_t)N * H * 4, hipMemcpyDeviceToHost));
+      if (memcmp(pay, pay_ref, rows * pb) != 0) return fail("unpacked payload differs");
+      if (dtype != LL_MOE_BF16 && memcmp(sc, sc_ref, rows * ns * 4) != 0)
+        return fail("unpacked scales differ");
+      if (memcmp(src, src_ref, rows * 4) != 0) return fail("unpacked sources differ");
+      if (memcmp(counts, counts_ref, E * 4) != 0) return fail("unpacked counts differ");
+      if (memcmp(got, image, total) != 0) return fail("two-phase layout differs");
+      if (memcmp(out, ref, (size_t)N * H * 4) != 0) return fail("two-phase combine bits differ");
+    }
+    hipFree(d_pay), hipFree(d_sc), hipFree(d_src), hipFree(d_cnt), hipFree(d_status);
+    free(pay), free(pay_ref), free(sc), free(sc_ref), free(src), free(src_ref);
   }
   hipFree(d_lay);
   hipFree(d_x);

@@ -5,7 +5,8 @@ no Python or PyTorch in the process.
 The host checks (layout sizes and offsets against the oracle, status strings,
 argument errors) need no GPU; the gpu checks run a small dispatch and combine
 on both parities and compare the whole layout byte for byte and the combine
-output bit for bit with the oracle."""
+output bit for bit with the oracle, then the expert side and the two-phase
+combine the same way."""
 import os
 import shutil
 import subprocess
@@ -47,5 +48,6 @@ def test_c_consumer_host(consumer):
 
 @pytest.mark.gpu
 def test_c_consumer_gpu(consumer):
-    print("C consumer: dispatch+combine N=37 h=384 E=9 K=3, bf16 and fp8, both parities", flush=True)
+    print("C consumer: dispatch, combine, expert side and two-phase combine, N=37 h=384 E=9 K=3, "
+          "bf16 and fp8, both parities", flush=True)
     _run(consumer, "gpu")
