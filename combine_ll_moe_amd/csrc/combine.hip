@@ -13,10 +13,11 @@
 // Design on gfx950: one workgroup per (tile of consecutive tokens, run of
 // columns); the runs of a row are equal, one 16-byte chunk per thread
 // (kernels.h, combine_shape). It computes the tile's slots once (route.h);
-// then, token by token, every thread issues its topk 16-byte loads of bf16
-// expert rows at once (all outstanding together), folds them with
-// v_fma_f32 in k order, and writes 8 fp32 results as two 16-byte streaming
-// stores (gather.h). Workgroup 0 zeroes the other set's signal words.
+// then every thread issues its topk 16-byte loads of bf16 expert rows at
+// once (a tile of two tokens: both tokens' loads), folds them with
+// v_fma_f32 in k order, and writes 8 fp32 results per token as two 16-byte
+// streaming stores (gather.h). Workgroup 0 zeroes the other set's signal
+// words.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,28 +27,6 @@
 #include "gather.h"
 
 namespace llmoe {
-
-// Gather-reduce of token t (entry row i of the tile) over this thread's 8
-// columns: the rows of its picks from the tile's slots, then gather_fold.
-template <int MAXK, bool STREAM>
-__device__ __forceinline__ void combine_token(const CombineParams& P, const RouteShared& rs, int t,
-                                              int i, int c, int chunks) {
-  uint64_t row[MAXK];
-  bool routed[MAXK];
-  float w[MAXK];
-#pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    const int kk = k < P.topk ? k : 0;
-    const int s = rs.slot[i * P.topk + kk];
-    routed[k] = k < P.topk && s >= 0;
-    row[k] = (uint64_t)(routed[k] ? rs.expert[i * P.topk + kk] : 0) * (uint64_t)P.max_tokens +
-             (uint64_t)(routed[k] ? s : 0);
-    w[k] = P.w[(uint64_t)t * P.topk + kk];
-  }
-  gather_fold<MAXK, STREAM>(reinterpret_cast<const g32x4*>(P.y), row, routed, w, c, chunks,
-                            reinterpret_cast<gf32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) +
-                                2 * (uint64_t)c);
-}
 
 template <int MAXK, bool STREAM>
 __global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const CombineParams P) {
@@ -74,7 +53,23 @@ __global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const Combine
   const int chunks = P.hidden / 8;
   const int c = sl * (int)blockDim.x + tid;
   if (c >= chunks) return;
-  for (int t = t0; t < t1; ++t) combine_token<MAXK, STREAM>(P, rs, t, t - t0, c, chunks);
+  // token i of the tile: its picks' rows from the tile's slots
+  auto tok = [&](int i, uint64_t (&row)[MAXK], bool (&routed)[MAXK], float (&w)[MAXK]) {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      const int kk = k < P.topk ? k : 0;
+      const int s = rs.slot[i * P.topk + kk];
+      routed[k] = k < P.topk && s >= 0;
+      row[k] = (uint64_t)(routed[k] ? rs.expert[i * P.topk + kk] : 0) * (uint64_t)P.max_tokens +
+               (uint64_t)(routed[k] ? s : 0);
+      w[k] = P.w[(uint64_t)(t0 + i) * P.topk + kk];
+    }
+  };
+  auto out = [&](int i) {
+    return reinterpret_cast<gf32x4*>(P.out) + (uint64_t)(t0 + i) * (uint64_t)(chunks * 2) +
+           2 * (uint64_t)c;
+  };
+  gather_tile<MAXK, STREAM>(reinterpret_cast<const g32x4*>(P.y), t1 - t0, c, chunks, tok, out);
 }
 
 template <bool STREAM>

@@ -12,7 +12,7 @@
 //    (put_chunks, as the dispatch writes batches below 64 MiB). No loads of
 //    x, no routing and no count publish.
 //  - gather_rows: the combine's gather alone. Each token folds the listed
-//    expert-output rows through the combine's own gather_fold, in the
+//    expert-output rows through the combine's own gather_tile, in the
 //    combine's launch shape, with no routing prologue.
 // None of them is part of the step.
 #include <hip/hip_runtime.h>
@@ -200,7 +200,7 @@ hipError_t launch_store_rows_policy(int policy, uint8_t* base, const int64_t* of
 }
 
 // The combine's work items, rows handed in: workgroup -> (tile of tokens,
-// run of columns), each token's picks folded by gather_fold. A row outside
+// run of columns), the tile's picks gathered and folded by gather_tile. A row outside
 // [0, y_rows) (a masked pick is -1) takes no part.
 template <int MAXK, bool STREAM>
 __global__ void __launch_bounds__(kCombineMaxBlock)
@@ -213,10 +213,8 @@ __global__ void __launch_bounds__(kCombineMaxBlock)
   const int c = sl * (int)blockDim.x + threadIdx.x;
   if (t0 >= num_tokens || c >= chunks) return;
   const int t1 = t0 + tile < num_tokens ? t0 + tile : num_tokens;
-  for (int t = t0; t < t1; ++t) {
-    uint64_t row[MAXK];
-    bool routed[MAXK];
-    float w[MAXK];
+  auto tok = [&](int i, uint64_t (&row)[MAXK], bool (&routed)[MAXK], float (&w)[MAXK]) {
+    const int t = t0 + i;
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
       const int kk = k < topk ? k : 0;
@@ -225,9 +223,11 @@ __global__ void __launch_bounds__(kCombineMaxBlock)
       row[k] = routed[k] ? (uint64_t)r : 0;
       w[k] = wt[(uint64_t)t * topk + kk];
     }
-    gather_fold<MAXK, STREAM>(y, row, routed, w, c, chunks,
-                              out + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c);
-  }
+  };
+  auto dst = [&](int i) {
+    return out + (uint64_t)(t0 + i) * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
+  };
+  gather_tile<MAXK, STREAM>(y, t1 - t0, c, chunks, tok, dst);
 }
 
 template <bool STREAM>
@@ -314,7 +314,7 @@ extern "C" int ll_moe_diag_gather_rows(const void* y, long long y_rows, int hidd
                                        const int32_t* rows, const float* weights, int num_tokens,
                                        int topk, float* out, hipStream_t stream) {
   if (num_tokens < 0 || hidden < 8 || hidden % 8 != 0 || topk < 1 || topk > LL_MOE_MAX_TOPK ||
-      y_rows < 0)
+      y_rows < 1)  // a token with no pick in range still loads row 0
     return LL_MOE_INVALID_ARGUMENT;
   if (num_tokens == 0) return LL_MOE_SUCCESS;
   if (!y || !rows || !weights || !out || !aligned(y, 16) || !aligned(out, 16) ||

@@ -160,7 +160,8 @@ int ll_moe_diag_store_rows(void* base, const int64_t* row_offsets, int nrows, in
  *   weights: device, fp32 [num_tokens, topk].
  *   out:     device, fp32 [num_tokens, hidden], 16-byte aligned.
  * INVALID_ARGUMENT: num_tokens < 0, hidden not a positive multiple of 8,
- * topk outside [1, LL_MOE_MAX_TOPK], y_rows < 0, a null or misaligned
+ * topk outside [1, LL_MOE_MAX_TOPK], y_rows < 1 (a token with no pick in
+ * range still loads row 0, its value unused), a null or misaligned
  * pointer. num_tokens == 0 enqueues nothing.
  */
 int ll_moe_diag_gather_rows(const void* y, long long y_rows, int hidden, const int32_t* rows,

@@ -136,6 +136,20 @@ def test_store_probe_rejects_bad_arguments(case):
     assert rc == ll.INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", [
+    dict(y_rows=0), dict(y_rows=-1), dict(n=-1), dict(hidden=0), dict(hidden=1020),
+    dict(topk=0), dict(topk=17), dict(y=0), dict(y=FAKE + 8), dict(rows=0), dict(w=0),
+    dict(out=0), dict(out=FAKE + 4),
+])
+def test_gather_probe_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(y=FAKE, y_rows=64, hidden=1024, rows=FAKE, w=FAKE, n=16, topk=8, out=FAKE)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_diag_gather_rows", a["y"], a["y_rows"], a["hidden"], a["rows"],
+                       a["w"], a["n"], a["topk"], a["out"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 BIG = 1 << 36  # far above any FAKE layout: never overlaps it
 
 
