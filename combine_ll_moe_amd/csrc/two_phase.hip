@@ -228,10 +228,13 @@ hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stre
   return hipGetLastError();
 }
 
-// Token t's gather-fold over this thread's 8 columns, once the flags are
-// up. Lane k of the wavefront holds pick k's expert (e_l, or -1 when masked)
-// and weight (w_l); a masked pick borrows a routed pick's row so that the
-// loads stay unconditional, and its value is never used.
+// The gather-fold of NT consecutive tokens t0.. over this thread's 8
+// columns, once the flags are up. Lane k of the wavefront holds token i's
+// pick k's expert (e_l[i], or -1 when masked) and weight (w_l[i]); every
+// load is issued before any is used; a masked pick borrows a routed pick's
+// row of its token (its expert-0 row when none is routed) so that the loads
+// stay unconditional, with no branch between them, and its value is never
+// used.
 //
 // The staged payload is read with device-coherent buffer loads (sc1): like
 // the flag polls, they are served at device scope and never from a stale L2
@@ -240,56 +243,60 @@ hipError_t launch_combine_send(const SendParams& p, int blocks, hipStream_t stre
 // That takes the place of an acquire fence, which would invalidate the
 // XCD's L2 once per wavefront and token (14 us of an 18 us launch at 128
 // tokens). The descriptor of pick k covers its one staging row.
-template <int MAXK, bool STREAM>
-__device__ __forceinline__ void fold_token(const RecvParams& P, int t, int c, int e_l, float w_l) {
+template <int NT, int MAXK, bool STREAM>
+__device__ __forceinline__ void fold_tokens(const RecvParams& P, int t0, int c,
+                                            const int (&e_l)[NT], const float (&w_l)[NT]) {
   constexpr int kPolicy = STREAM ? kCachePolicySc1 | kCachePolicyNt : kCachePolicySc1;
-  uint64_t row[MAXK];
-  bool routed[MAXK];
-  float w[MAXK];
+  bool routed[NT][MAXK];
+  float w[NT][MAXK];
+  u32x4 v[NT][MAXK];
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    const int e = __builtin_amdgcn_readlane(e_l, k < P.topk ? k : 0);
-    routed[k] = k < P.topk && e >= 0;
-    row[k] = (uint64_t)(routed[k] ? e : 0) * (uint64_t)P.max_tokens + (uint64_t)t;
-    w[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), k < P.topk ? k : 0));
-  }
-  bool any = false;
-  uint64_t fallback = 0;
+  for (int i = 0; i < NT; ++i) {
+    uint64_t row[MAXK];
 #pragma unroll
-  for (int k = MAXK - 1; k >= 0; --k) {
-    fallback = routed[k] ? row[k] : fallback;
-    any = any || routed[k];
-  }
-  float acc[8];
+    for (int k = 0; k < MAXK; ++k) {
+      const int e = __builtin_amdgcn_readlane(e_l[i], k < P.topk ? k : 0);
+      routed[i][k] = k < P.topk && e >= 0;
+      row[k] = (uint64_t)(routed[i][k] ? e : 0) * (uint64_t)P.max_tokens + (uint64_t)(t0 + i);
+      w[i][k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l[i]),
+                                                         k < P.topk ? k : 0));
+    }
+    uint64_t fallback = (uint64_t)(t0 + i);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  if (any) {
-    u32x4 v[MAXK];
+    for (int k = MAXK - 1; k >= 0; --k) fallback = routed[i][k] ? row[k] : fallback;
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
       const BufRsrc rsrc = message_rsrc(
-          const_cast<uint8_t*>(P.stage) + (routed[k] ? row[k] : fallback) * P.comb_bytes,
+          const_cast<uint8_t*>(P.stage) + (routed[i][k] ? row[k] : fallback) * P.comb_bytes,
           P.comb_bytes);
-      v[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, 4 + 16 * c, 0, kPolicy);
-    }
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const uint32_t q[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float a = __builtin_fmaf(w[k], __uint_as_float(q[h] << 16), acc[2 * h]);
-        const float b = __builtin_fmaf(w[k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
-        acc[2 * h] = routed[k] ? a : acc[2 * h];
-        acc[2 * h + 1] = routed[k] ? b : acc[2 * h + 1];
-      }
+      v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, 4 + 16 * c, 0, kPolicy);
     }
   }
   const int chunks = P.hidden / 8;
-  f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)t * (uint64_t)(chunks * 2) + 2 * (uint64_t)c;
-  const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
-  const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
-  __builtin_nontemporal_store(lo, o);
-  __builtin_nontemporal_store(hi, o + 1);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      const uint32_t q[4] = {v[i][k].x, v[i][k].y, v[i][k].z, v[i][k].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float a = __builtin_fmaf(w[i][k], __uint_as_float(q[h] << 16), acc[2 * h]);
+        const float b =
+            __builtin_fmaf(w[i][k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
+        acc[2 * h] = routed[i][k] ? a : acc[2 * h];
+        acc[2 * h + 1] = routed[i][k] ? b : acc[2 * h + 1];
+      }
+    }
+    f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)(t0 + i) * (uint64_t)(chunks * 2) +
+               2 * (uint64_t)c;
+    const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
+    const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
+    __builtin_nontemporal_store(lo, o);
+    __builtin_nontemporal_store(hi, o + 1);
+  }
 }
 
 template <int MAXK, bool STREAM>
@@ -374,19 +381,32 @@ __global__ void __launch_bounds__(kCombineMaxBlock) combine_recv_kernel(const Re
     const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
     const int c = sl * (int)blockDim.x + tid;
     // A wavefront wholly past the row has nothing to do. In the others every
-    // lane loads its pick, also lanes past the row: fold_token reads picks
+    // lane loads its pick, also lanes past the row: fold_tokens reads picks
     // from lanes 0..topk-1 with readlane, which ignores the execution mask,
-    // so those lanes must hold this token's values.
+    // so those lanes must hold the tokens' values.
     if (sl * (int)blockDim.x + (tid & ~(kWave - 1)) >= chunks) continue;
-    for (int t = t0; t < t1; ++t) {
-      int e_l = -1;
-      float w_l = 0.0f;
+    auto pick = [&](int t, int& e_l, float& w_l) {
+      e_l = -1;
+      w_l = 0.0f;
       if (lane < P.topk) {
         const int e = P.idx[(uint64_t)t * P.topk + lane];
         e_l = e >= 0 && e < E ? e : -1;
         w_l = P.w[(uint64_t)t * P.topk + lane];
       }
-      if (c < chunks) fold_token<MAXK, STREAM>(P, t, c, e_l, w_l);
+    };
+    if (MAXK <= 8 && t1 - t0 == 2) {  // both tokens' loads in flight, as the fused combine
+      int e_l[2];
+      float w_l[2];
+      pick(t0, e_l[0], w_l[0]);
+      pick(t0 + 1, e_l[1], w_l[1]);
+      if (c < chunks) fold_tokens<2, MAXK, STREAM>(P, t0, c, e_l, w_l);
+    } else {
+      for (int t = t0; t < t1; ++t) {
+        int e_l[1];
+        float w_l[1];
+        pick(t, e_l[0], w_l[0]);
+        if (c < chunks) fold_tokens<1, MAXK, STREAM>(P, t, c, e_l, w_l);
+      }
     }
   }
 }
