@@ -30,6 +30,7 @@ def _run_step(st: Step, q, x, idx, wt, y, y_dev=None):
     st.check_signals()
     diff = check_combine(out, ref)
     assert diff == 0, f"{diff} combine outputs differ in bits"
+    return out
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "decode_fp8", "wide_zipf", "worst_fill"])
@@ -143,6 +144,27 @@ def test_combine_column_runs(shape):
     st = Step(w, full_image=False)
     for q in (0, 1):
         _run_step(st, q, x, idx, wt, y)
+
+
+@pytest.mark.parametrize("n", [64, 2048])
+def test_fully_masked_tokens(n):
+    """Tokens whose every pick is masked (out of range or -1) write +0.0f and
+    load nothing that matters: alone, as the first or second token of a
+    two-token tile (N=2048), and both tokens of a tile."""
+    w = W.Workload("masked", n, 64, 8, 4, W.BF16, "uniform", seed=n)
+    rng = np.random.default_rng(n)
+    idx = np.stack([rng.permutation(8)[:4] for _ in range(n)]).astype(np.int32)
+    for t in (0, 1, 5, 6, 7, n - 2, n - 1):  # tiles (0,1), (6,7), (n-2,n-1) whole; 5 alone
+        idx[t] = -1
+    idx[9] = [8, -1, 100, -5]
+    x, wt = W.tokens(w), W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    say(f"[parity] fully masked tokens: N={n}")
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        out = _run_step(st, q, x, idx, wt, y)
+        for t in (0, 1, 5, 6, 7, 9, n - 2, n - 1):
+            assert not out[t].view(np.uint32).any(), f"token {t} is not +0.0f"
 
 
 def test_masked_repeated_and_overflowing_picks():
