@@ -97,7 +97,7 @@ struct UnpackParams {              // expert side of the dispatch
   uint32_t row_bytes;              // payload bytes of one unpacked row
   int expected;                    // messages the step routes
   int max_spins;                   // polls of the counts before the wait gives up
-  int wide;                        // 64 MiB of messages or more: more loads in flight per lane, streaming payload stores
+  int wide;                        // 64 MiB of messages or more: more loads in flight per lane
 };
 
 // The two-phase combine's expert side keeps every expert's count in LDS.

@@ -43,8 +43,11 @@ namespace llmoe {
 // with non-temporal stores, so that they do not evict from the MALL the
 // receive rows still to be read (for 64 MiB or more: 1024 tokens of 7168
 // columns unpacked in 39.0 against 45.1 us, and a dispatch followed by its
-// unpack in 67.5 against 76.8; at 128 tokens plain stores keep the
-// dispatch-and-unpack step shorter, 15.3 against 15.9 us).
+// unpack in 67.5 against 76.8). Below that size fp8 payloads stream too
+// (128 tokens of 7168 columns: unpack 5.1 against 5.5 us, dispatch and
+// unpack 13.2 against 13.5), bf16 ones do not (plain stores keep that pair
+// shorter, 15.3 against 15.9 us, though the unpack alone is 6.0 against
+// 6.6).
 template <int KROUND, bool STREAM_OUT>
 __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackParams P) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
@@ -163,6 +166,9 @@ __global__ void __launch_bounds__(kSendBlock) dispatch_recv_kernel(const UnpackP
 hipError_t launch_dispatch_recv(const UnpackParams& p, int blocks, hipStream_t stream) {
   if (p.wide)
     dispatch_recv_kernel<16, true>
+        <<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
+  else if (p.fp8)
+    dispatch_recv_kernel<8, true>
         <<<blocks, kSendBlock, count_prefix_bytes(p.num_experts), stream>>>(p);
   else
     dispatch_recv_kernel<8, false>
