@@ -9,7 +9,6 @@ import re
 import pytest
 
 import oracle
-import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
