@@ -43,14 +43,16 @@ __device__ __forceinline__ void store_b32(uint32_t v, BufRsrc r, uint32_t off) {
 
 // NSTAGE * blockDim 16-byte chunks of a row into registers, from chunk
 // `base` on (thread i takes chunks base + i + u * blockDim); unconditional
-// loads with the index clamped into the row.
-template <int NSTAGE>
+// loads with the index clamped into the row. STREAM: non-temporal loads,
+// for rows read once.
+template <int NSTAGE, bool STREAM = false>
 __device__ __forceinline__ void load_row(u32x4 (&r)[NSTAGE], const u32x4* __restrict__ xr,
                                          int chunks, int base = 0) {
 #pragma unroll
   for (int u = 0; u < NSTAGE; ++u) {
     const int j = base + (int)threadIdx.x + u * (int)blockDim.x;
-    r[u] = xr[j < chunks ? j : chunks - 1];
+    const u32x4* src = xr + (j < chunks ? j : chunks - 1);
+    r[u] = STREAM ? __builtin_nontemporal_load(src) : *src;
   }
 }
 
