@@ -31,7 +31,8 @@ workload's; "configs" holds the same block for every workload timed:
   floors     hand-written probes timed like the step: the dispatch's stores
              alone over its exact destination rows and the combine's gather
              alone over its exact rows, neither with routing or publish;
-  ceilings   contiguous 1 GiB write / read / copy by hand-written kernels;
+  ceilings   contiguous 1 GiB write / read / copy by hand-written kernels,
+             and a fold reading 4 bytes per byte written (the combine's mix);
   cpu_baseline  the CPU oracle on the headline workload, one host core.
 """
 import argparse
@@ -341,23 +342,28 @@ class Clock:
 
 def ceilings(torch, ll, clock: Clock) -> dict:
     """Contiguous 1 GiB write, read and copy by the hand-written stream
-    probe, best over a few grid sizes and both load/store hints: the part's
-    practical HBM rates for this kind of access."""
+    probe, and its fold of 1 GiB read into 256 MiB written (4:1, the
+    combine's mix), best over a few grid sizes and both load/store hints:
+    the part's practical HBM rates for this kind of access."""
     dev = torch.device("cuda:0")
     a = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
     b = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
     ll.ll_moe_diag_stream(ll.PROBE_WRITE, False, a, None, CEILING_BYTES, 4096)
     torch.cuda.synchronize()
     res = {}
-    for mode, name, moved in ((ll.PROBE_WRITE, "write", 1), (ll.PROBE_READ, "read", 1),
-                              (ll.PROBE_COPY, "copy", 2)):
+    # (mode, name, bytes written or read, bytes moved per byte of that):
+    # fold4 reads the whole 1 GiB into a quarter of it, the combine's mix
+    for mode, name, nbytes, moved in (
+            (ll.PROBE_WRITE, "write", CEILING_BYTES, 1), (ll.PROBE_READ, "read", CEILING_BYTES, 1),
+            (ll.PROBE_COPY, "copy", CEILING_BYTES, 2),
+            (ll.PROBE_FOLD4, "fold4", CEILING_BYTES // 4, 5)):
         best = None
         for nt in (False, True):
             for blocks in (4096, 16384, 65536):
                 us = clock.per_call(f"ceiling {name} nt={int(nt)} blocks={blocks}",
-                                    lambda s: ll.ll_moe_diag_stream(mode, nt, b, a, CEILING_BYTES,
+                                    lambda s: ll.ll_moe_diag_stream(mode, nt, b, a, nbytes,
                                                                     blocks), 5)
-                gbs = moved * CEILING_BYTES / (us * 1e-6) / 1e9
+                gbs = moved * nbytes / (us * 1e-6) / 1e9
                 if best is None or gbs > best["gbs"]:
                     best = {"gbs": round(gbs, 1), "us": round(us, 2), "non_temporal": nt,
                             "blocks": blocks}

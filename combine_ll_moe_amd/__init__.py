@@ -40,6 +40,7 @@ INVALID_USAGE = 5
 PROBE_WRITE = 0
 PROBE_READ = 1
 PROBE_COPY = 2
+PROBE_FOLD4 = 3
 PROBE_ROWS_GROUP = 0
 PROBE_ROWS_WAVE = 1
 PROBE_ROWS_DIRECT = 2
@@ -195,7 +196,8 @@ def ll_moe_diag_watch(layout, max_tokens: int, num_tokens: int, hidden: int, num
 
 def ll_moe_diag_stream(mode: int, non_temporal: bool, dst, src, nbytes: int, blocks: int,
                        stream=None) -> None:
-    """Measurement probe: a contiguous write / read / copy of nbytes."""
+    """Measurement probe: a contiguous write / read / copy of nbytes, or a
+    fold of 4 * nbytes read into nbytes written."""
     _check(_lib.ll_moe_diag_stream(mode, int(bool(non_temporal)), _ptr(dst), _ptr(src), nbytes,
                                    blocks, _stream(stream)), "ll_moe_diag_stream")
 

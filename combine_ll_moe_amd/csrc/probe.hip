@@ -3,7 +3,9 @@
 // that the path can be placed against what the part itself does.
 //
 //  - stream: a contiguous write, read or copy of a large buffer, 16-byte
-//    accesses, four in flight per thread: the practical HBM ceilings.
+//    accesses, four in flight per thread: the practical HBM ceilings; and a
+//    fold that reads four bytes for every byte it writes (the combine's
+//    proportions at top-k 8), sixteen loads in flight per thread.
 //  - store_rows: the dispatch's stores alone. Every listed destination row
 //    receives row_bytes bytes of a pattern through one of the dispatch's
 //    own store routines: from an LDS buffer by workgroup (copy_message) or
@@ -30,11 +32,13 @@ namespace {
 
 constexpr int kProbeBlock = 256;
 constexpr int kStreamUnroll = 4;
+constexpr int kFoldSources = 4;  // source regions of the fold: 4 bytes read per byte written
 constexpr int kMaxRowsPerBlock = kProbeBlock;
 
 // Workgroup b streams tiles b, b + grid, ... of kProbeBlock * kStreamUnroll
 // 16-byte chunks (16 KiB), each tile contiguous: every wavefront store or
-// load covers 1 KiB, and a workgroup's four in flight cover 16 KiB.
+// load covers 1 KiB, and a workgroup's four in flight cover 16 KiB (the
+// fold: the same tile of each of its four source regions, 64 KiB).
 template <int MODE, bool NT>
 __global__ void __launch_bounds__(kProbeBlock)
     stream_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, uint64_t n,
@@ -52,6 +56,28 @@ __global__ void __launch_bounds__(kProbeBlock)
             __builtin_nontemporal_store(v, dst + j);
           else
             dst[j] = v;
+        }
+      }
+    } else if constexpr (MODE == LL_MOE_PROBE_FOLD4) {
+      // dst[j] = src[j] + src[n + j] + src[2n + j] + src[3n + j], lane-wise
+      u32x4 v[kStreamUnroll][kFoldSources];
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const uint64_t j = t0 + (uint64_t)u * kProbeBlock + threadIdx.x;
+        const uint64_t jj = j < n ? j : n - 1;
+#pragma unroll
+        for (int k = 0; k < kFoldSources; ++k)
+          v[u][k] = NT ? __builtin_nontemporal_load(src + k * n + jj) : src[k * n + jj];
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const uint64_t j = t0 + (uint64_t)u * kProbeBlock + threadIdx.x;
+        const u32x4 f = v[u][0] + v[u][1] + v[u][2] + v[u][3];
+        if (j < n) {
+          if (NT)
+            __builtin_nontemporal_store(f, dst + j);
+          else
+            dst[j] = f;
         }
       }
     } else {
@@ -258,7 +284,8 @@ using namespace llmoe;
 
 extern "C" int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const void* src,
                                   size_t bytes, int blocks, hipStream_t stream) {
-  if (mode != LL_MOE_PROBE_WRITE && mode != LL_MOE_PROBE_READ && mode != LL_MOE_PROBE_COPY)
+  if (mode != LL_MOE_PROBE_WRITE && mode != LL_MOE_PROBE_READ && mode != LL_MOE_PROBE_COPY &&
+      mode != LL_MOE_PROBE_FOLD4)
     return LL_MOE_INVALID_ARGUMENT;
   if (blocks < 1 || bytes % 16 != 0) return LL_MOE_INVALID_ARGUMENT;
   if (bytes == 0) return LL_MOE_SUCCESS;
@@ -272,8 +299,10 @@ extern "C" int ll_moe_diag_stream(int mode, int non_temporal, void* dst, const v
     e = launch_stream_mode<LL_MOE_PROBE_WRITE>(non_temporal != 0, d, s, n, blocks, stream);
   else if (mode == LL_MOE_PROBE_READ)
     e = launch_stream_mode<LL_MOE_PROBE_READ>(non_temporal != 0, d, s, n, blocks, stream);
-  else
+  else if (mode == LL_MOE_PROBE_COPY)
     e = launch_stream_mode<LL_MOE_PROBE_COPY>(non_temporal != 0, d, s, n, blocks, stream);
+  else
+    e = launch_stream_mode<LL_MOE_PROBE_FOLD4>(non_temporal != 0, d, s, n, blocks, stream);
   return from_hip(e);
 }
 

@@ -92,14 +92,21 @@ int ll_moe_diag_watch(const void* layout, int max_tokens, int num_tokens, int hi
 #define LL_MOE_PROBE_WRITE 0  /* dst := a pattern */
 #define LL_MOE_PROBE_READ 1   /* read src (one word of dst may be written) */
 #define LL_MOE_PROBE_COPY 2   /* dst := src */
+#define LL_MOE_PROBE_FOLD4 3  /* dst := lane-wise uint32 sum of 4 source regions */
 
 /*
  * ll_moe_diag_stream — a contiguous stream of `bytes` bytes: write, read or
  * copy (mode above), 16-byte accesses, four in flight per thread, `blocks`
  * workgroups of 256 threads striding over the buffer; non_temporal != 0
- * gives the accesses the streaming (non-temporal) hint.
+ * gives the accesses the streaming (non-temporal) hint. FOLD4 writes
+ * `bytes` bytes and reads four times as many: 16-byte chunk j of dst
+ * becomes the lane-wise wrapping uint32 sum of chunk j of the four
+ * consecutive `bytes`-byte regions of src, sixteen loads in flight per
+ * thread. That is the combine's mix of traffic at top-k 8 (16h bytes of
+ * bf16 rows read per 4h bytes of fp32 output written).
  *   dst: device, 16-byte aligned, `bytes` bytes (READ: at least 16 bytes).
- *   src: device, 16-byte aligned, `bytes` bytes (READ and COPY).
+ *   src: device, 16-byte aligned, `bytes` bytes (READ and COPY), 4 * `bytes`
+ *        bytes (FOLD4).
  * INVALID_ARGUMENT: bytes % 16 != 0, blocks < 1, a null or misaligned
  * pointer the mode needs, an unknown mode. bytes == 0 enqueues nothing.
  */

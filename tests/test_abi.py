@@ -149,6 +149,20 @@ def test_gather_probe_rejects_bad_arguments(case):
     assert rc == ll.INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("case", [
+    dict(mode=4), dict(mode=-1), dict(nbytes=1000), dict(blocks=0), dict(dst=0),
+    dict(dst=FAKE + 4), dict(src=0), dict(src=FAKE + 8), dict(mode=1, src=0),
+    dict(mode=2, src=FAKE + 4),
+])
+def test_stream_probe_rejects_bad_arguments(case):
+    import combine_ll_moe_amd as ll
+    a = dict(mode=3, nt=0, dst=FAKE, src=FAKE, nbytes=1024, blocks=4)
+    a.update(case)
+    rc = ll.raw_status("ll_moe_diag_stream", a["mode"], a["nt"], a["dst"], a["src"], a["nbytes"],
+                       a["blocks"], None)
+    assert rc == ll.INVALID_ARGUMENT
+
+
 BIG = 1 << 36  # far above any FAKE layout: never overlaps it
 
 

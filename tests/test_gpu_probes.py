@@ -114,3 +114,18 @@ def test_stream_copy_reproduces_its_source(nt):
     torch.cuda.synchronize()
     words = dst.cpu().numpy().view(np.uint32).reshape(-1, 4)
     assert (words[:, 0] == 0x5A5A5A5A).all() and (words[:, 1] == 0x5A5A5A5B).all()
+
+
+@pytest.mark.parametrize("nt", [False, True])
+def test_stream_fold_sums_its_four_regions(nt):
+    n = (1 << 20) + 48  # bytes written: several tiles and a ragged tail
+    src = torch.randint(0, 256, (4 * n,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(n + 16, dtype=torch.uint8, device=DEV)
+    say(f"[probe] stream fold4 nt={nt} bytes={n}")
+    ll.ll_moe_diag_stream(ll.PROBE_FOLD4, nt, dst, src, n, 37)
+    torch.cuda.synchronize()
+    words = src.cpu().numpy().view(np.uint32).reshape(4, -1).astype(np.uint64)
+    want = (words.sum(axis=0) & 0xFFFFFFFF).astype(np.uint32)
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:n].view(np.uint32), want)
+    assert not got[n:].any()  # nothing past the bytes asked for
