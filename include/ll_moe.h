@@ -164,7 +164,11 @@ int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int hidden,
  *   expert_out:   device, bf16 [num_experts * max_tokens, hidden], 16-byte
  *                 aligned, in receive-slot order: row e * max_tokens + j is
  *                 expert e's output for the j-th message it received.
- *                 Only rows of routed (t, k) are read.
+ *                 Only rows of routed (t, k) contribute. Every load is
+ *                 unconditional: a pick that is not routed reads a routed
+ *                 pick's row of its token instead, or row 0 when none is
+ *                 routed, and that value is never used. No row outside
+ *                 the buffer is read.
  *   topk_idx:     device, int32 [num_tokens, topk] (the dispatch routing).
  *   topk_weights: device, fp32 [num_tokens, topk].
  *   out:          device, fp32 [num_tokens, hidden], 16-byte aligned; may
