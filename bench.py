@@ -959,6 +959,15 @@ def main():
         clock = Clock(torch, torch.cuda.current_stream(), reset)
         ceil = ceilings(torch, ll, clock)
         print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
+        # each kernel's algorithmic rate against the practical ceiling of
+        # its kind of traffic: the dispatch mostly writes (for 1024 tokens of
+        # 7168 columns, 14.7 of its 146.9 MB are reads of x); the combine
+        # reads 4 bytes per byte written at top-k 8, as the fold does
+        for r in results.values():
+            f = r["kernel_fracs"]
+            r["kernel_vs_ceilings"] = {
+                "dispatch_vs_write": round(f["dispatch"] * HBM_PEAK_GBS / ceil["write"]["gbs"], 4),
+                "combine_vs_fold4": round(f["combine"] * HBM_PEAK_GBS / ceil["fold4"]["gbs"], 4)}
 
     h = results[headline]
     result = {
@@ -986,6 +995,7 @@ def main():
         "two_phase_combine": h["two_phase_combine"],
         "expert_side": h["expert_side"],
         "roofline": h["roofline"],
+        "kernel_vs_ceilings": h.get("kernel_vs_ceilings"),
         "cpu_baseline": None,
         "configs": {n: {k: v for k, v in r.items() if k != "profile_regions"}
                     for n, r in results.items()},
