@@ -46,13 +46,13 @@
 #include <stdint.h>
 
 #include "expert.h"
+#include "gather.h"
 #include "kernels.h"
 #include "message.h"
 #include "route.h"
 
 namespace llmoe {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Rows at or above this many bytes go out with whole-cache-line lane
 // mapping (mostly HBM-bound writes); smaller ones stay in the caches.
@@ -273,30 +273,10 @@ __device__ __forceinline__ void fold_tokens(const RecvParams& P, int t0, int c,
     }
   }
   const int chunks = P.hidden / 8;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const uint32_t q[4] = {v[i][k].x, v[i][k].y, v[i][k].z, v[i][k].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float a = __builtin_fmaf(w[i][k], __uint_as_float(q[h] << 16), acc[2 * h]);
-        const float b =
-            __builtin_fmaf(w[i][k], __uint_as_float(q[h] & 0xFFFF0000u), acc[2 * h + 1]);
-        acc[2 * h] = routed[i][k] ? a : acc[2 * h];
-        acc[2 * h + 1] = routed[i][k] ? b : acc[2 * h + 1];
-      }
-    }
-    f32x4* o = reinterpret_cast<f32x4*>(P.out) + (uint64_t)(t0 + i) * (uint64_t)(chunks * 2) +
-               2 * (uint64_t)c;
-    const f32x4 lo = {acc[0], acc[1], acc[2], acc[3]};
-    const f32x4 hi = {acc[4], acc[5], acc[6], acc[7]};
-    __builtin_nontemporal_store(lo, o);
-    __builtin_nontemporal_store(hi, o + 1);
-  }
+  fold_store<NT, MAXK>(v, routed, w, [&](int i) {
+    return reinterpret_cast<gf32x4*>(P.out) + (uint64_t)(t0 + i) * (uint64_t)(chunks * 2) +
+           2 * (uint64_t)c;
+  });
 }
 
 template <int MAXK, bool STREAM>
