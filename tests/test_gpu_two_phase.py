@@ -318,6 +318,28 @@ def test_two_phase_masked_entries():
         assert (out[41].view(np.uint32) == 0).all()
 
 
+@pytest.mark.parametrize("n", [64, 2048])
+def test_two_phase_fully_masked_tokens(n):
+    """Tokens whose every pick is masked write +0.0f through the two-phase
+    combine too: alone, as the first or second token of a two-token tile
+    (N=2048 with 8 columns of chunks: one run per row, so tiles of two), and
+    both tokens of a tile."""
+    w = W.Workload("masked", n, 64, 8, 4, W.BF16, "uniform", seed=n + 1)
+    rng = np.random.default_rng(n + 1)
+    idx = np.stack([rng.permutation(8)[:4] for _ in range(n)]).astype(np.int32)
+    for t in (0, 1, 5, 6, 7, n - 2, n - 1):  # tiles (0,1), (6,7), (n-2,n-1) whole; 5 alone
+        idx[t] = -1
+    idx[9] = [8, -1, 100, -5]
+    x, wt = W.tokens(w), W.weights(w)
+    y = W.expert_outputs(w, filled_mask(w, idx))
+    say(f"[two-phase] fully masked tokens: N={n}")
+    st = Step(w, full_image=True)
+    for q in (0, 1):
+        out = _two_phase_step(st, q, x, idx, wt, y)
+        for t in (0, 1, 5, 6, 7, 9, n - 2, n - 1):
+            assert not out[t].view(np.uint32).any(), f"token {t} is not +0.0f"
+
+
 @pytest.mark.parametrize("block", range(2))
 def test_two_phase_random_shapes(block):
     """20 seeded random cases (10 per block; any dtype, hidden, expert count,
