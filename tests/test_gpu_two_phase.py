@@ -3,6 +3,8 @@ flags, then the token side's bounded wait and fold) through the C ABI,
 against the oracle on the same seeded inputs: staging rows and signal words
 byte for byte (the whole layout where the image is small), the folded
 output bit for bit, and equal to the one-shot combine's output."""
+import os
+
 import numpy as np
 import pytest
 
@@ -351,11 +353,7 @@ def test_two_phase_random_shapes(block):
     for case in range(10):
         rng = np.random.default_rng(3000 + 10 * block + case)
         w, idx = random_case(rng)
-        for t in range(idx.shape[0]):
-            _, first = np.unique(idx[t], return_index=True)
-            again = np.ones(idx.shape[1], bool)
-            again[first] = False
-            idx[t, again] = -1
+        idx = _mask_repeats(idx)
         pad = int(rng.choice([0, 16, 32, 48]))
         say(f"[two-phase] random case {10 * block + case}: N={w.num_tokens} cap={w.capacity} "
             f"h={w.hidden} E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad}")
@@ -365,5 +363,54 @@ def test_two_phase_random_shapes(block):
         y_dev = to_dev(y)
         for q in (0, 1):
             _two_phase_step(st, q, x, idx, wt, y, y_dev)
+        del st, y_dev
+        torch.cuda.empty_cache()
+
+
+# LL_MOE_SWEEP_CASES=n runs n more seeded random cases (seeds 20000 on); the
+# default runs none, so that the GPU suite stays short
+SWEEP_CASES = int(os.environ.get("LL_MOE_SWEEP_CASES", "0"))
+
+
+def _mask_repeats(idx):
+    """The two-phase combine takes at most one pick per (token, expert)."""
+    idx = idx.copy()
+    for t in range(idx.shape[0]):
+        _, first = np.unique(idx[t], return_index=True)
+        again = np.ones(idx.shape[1], bool)
+        again[first] = False
+        idx[t, again] = -1
+    return idx
+
+
+@pytest.mark.skipif(SWEEP_CASES == 0, reason="set LL_MOE_SWEEP_CASES for a longer random sweep")
+def test_random_sweep():
+    """A longer sweep of seeded random cases (the generator of the random
+    shape tests): both parities through the dispatch and the fused combine,
+    and every third case also through the two-phase combine with repeated
+    experts masked, each against the oracle."""
+    for seed in range(20000, 20000 + SWEEP_CASES):
+        rng = np.random.default_rng(seed)
+        w, idx = random_case(rng)
+        pad = int(rng.choice([0, 16, 32, 48]))
+        say(f"[sweep] case {seed}: N={w.num_tokens} cap={w.capacity} h={w.hidden} "
+            f"E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad}")
+        x, wt = W.tokens(w), W.weights(w)
+        y = W.expert_outputs(w, filled_mask(w, idx))
+        st = Step(w, full_image=False, base_pad=pad)
+        y_dev = to_dev(y)
+        for q in (0, 1):
+            st.dispatch(q, x, idx)
+            st.check_dispatch(q, idx)
+            out, ref = st.combine(q, y, idx, wt, y_dev=y_dev)
+            st.check_signals()
+            assert check_combine(out, ref) == 0, f"case {seed}: combine outputs differ"
+        if seed % 3 == 0:
+            idx1 = _mask_repeats(idx)
+            y1 = W.expert_outputs(w, filled_mask(w, idx1))
+            st1 = Step(w, full_image=False, base_pad=pad)
+            for q in (0, 1):
+                _two_phase_step(st1, q, x, idx1, wt, y1)
+            del st1
         del st, y_dev
         torch.cuda.empty_cache()
