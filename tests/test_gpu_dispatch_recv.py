@@ -4,6 +4,8 @@ on the same seeded inputs: payload rows, fp8 scales, source tokens and
 counts byte for byte, with sentinel-filled outputs so that a stray write
 shows; run after the dispatch in stream order, and started beside a held
 dispatch on a second stream."""
+import os
+
 import numpy as np
 import pytest
 
@@ -290,6 +292,34 @@ def test_unpack_random_shapes(block):
         say(f"[unpack] random case {10 * block + case}: N={w.num_tokens} cap={w.capacity} "
             f"h={w.hidden} E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad} "
             f"messages={expected}")
+        x = W.tokens(w)
+        st = Step(w, full_image=False, base_pad=pad)
+        for q in (0, 1):
+            outs = Outputs(w)
+            st.dispatch(q, x, idx)
+            outs.launch(st, q, expected)
+            _check(st, q, outs, expected, _filled(w, idx))
+        del st
+        torch.cuda.empty_cache()
+
+
+# LL_MOE_SWEEP_CASES=n runs n more seeded random cases (seeds 30000 on); the
+# default runs none, so that the GPU suite stays short
+SWEEP_CASES = int(os.environ.get("LL_MOE_SWEEP_CASES", "0"))
+
+
+@pytest.mark.skipif(SWEEP_CASES == 0, reason="set LL_MOE_SWEEP_CASES for a longer random sweep")
+def test_unpack_random_sweep():
+    """A longer sweep of seeded random cases through the dispatch and the
+    expert side, both parities, each against the oracle."""
+    for seed in range(30000, 30000 + SWEEP_CASES):
+        rng = np.random.default_rng(seed)
+        w, idx = random_case(rng)
+        pad = int(rng.choice([0, 16, 32, 48]))
+        _, cnt = oracle.route(idx, w.num_experts, w.capacity)
+        expected = int(cnt.sum())
+        say(f"[unpack sweep] case {seed}: N={w.num_tokens} cap={w.capacity} h={w.hidden} "
+            f"E={w.num_experts} K={w.topk} dtype={w.dtype} pad={pad} messages={expected}")
         x = W.tokens(w)
         st = Step(w, full_image=False, base_pad=pad)
         for q in (0, 1):
