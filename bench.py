@@ -33,6 +33,8 @@ workload's; "configs" holds the same block for every workload timed:
              alone over its exact rows, neither with routing or publish;
   ceilings   contiguous 1 GiB write / read / copy by hand-written kernels,
              and a fold reading 4 bytes per byte written (the combine's mix);
+  kernel_vs_ceilings  each kernel's rate over the ceiling of its kind of
+             traffic (the dispatch against write, the combine against fold);
   cpu_baseline  the CPU oracle on the headline workload, one host core.
 """
 import argparse
