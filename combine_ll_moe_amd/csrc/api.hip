@@ -30,19 +30,27 @@ uint32_t dispatch_lds_budget(int num_experts) {
   return 65536u - (uint32_t)sizeof(RouteShared) - 4u * (uint32_t)hist_cap_for(num_experts);
 }
 
-// The dispatch's routing prologue reads the table 4 entries per load when
-// the entries before the last tile would take more than two rounds of
-// single-entry loads (2048 entries each), the table is 16-byte aligned and
-// it is a whole number of 4-entry vectors: a late tile's later load rounds
-// otherwise queue behind the other workgroups' message stores (worst-fill:
-// prologues of up to 9 us; dispatch 28.9 -> 28.0 us). The combine keeps
-// single-entry loads: with 16-byte loads it measured slower at every size
-// (128 tokens of 7168 columns: 6.0 against 5.1 us).
+// The routing prologues read the table 4 entries per 16-byte load when it
+// is 16-byte aligned and a whole number of 4-entry vectors (vec_idx), with
+// few loads per thread and round: one in the register-path dispatch (128
+// tokens of 7168 columns: 5.18 against 5.40 us with 8 single-entry loads;
+// 512 tokens of 4096 columns, three rounds: 11.60 against 11.95), two in
+// the combine (128 tokens of 7168 columns, step 10.12 against 10.36 us with
+// both changes). The dispatch of 64 MiB or more reads 8 vectors per thread
+// and round, but only for tables of more than 4096 entries (wide_idx), so
+// that a late tile's later rounds do not queue behind the other
+// workgroups' message stores (1024 tokens of 8 picks: prologues of up to
+// 9 us; dispatch 28.9 -> 28.0 us); fewer loads per round measured slower
+// there (25.4 us with one, 24.7 with two, 24.4 with four or eight).
 constexpr int64_t kWideIdxEntries = 4096;
 
-int wide_idx_for(const int32_t* idx, int num_tokens, int topk) {
+int vec_idx_for(const int32_t* idx, int num_tokens, int topk) {
   const int64_t entries = (int64_t)num_tokens * topk;
-  return entries > kWideIdxEntries && entries % 4 == 0 && ((uintptr_t)idx & 15) == 0;
+  return entries % 4 == 0 && ((uintptr_t)idx & 15) == 0;
+}
+
+int wide_idx_for(const int32_t* idx, int num_tokens, int topk) {
+  return (int64_t)num_tokens * topk > kWideIdxEntries && vec_idx_for(idx, num_tokens, topk);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -141,6 +149,7 @@ extern "C" int ll_moe_dispatch(void* layout, int max_tokens, int num_tokens, int
   // from registers at the rows' own phase are faster (see
   // dispatch_direct_kernel).
   p.line_align = (uint64_t)num_tokens * (uint64_t)(topk + 1) * L.dispatch_msg >= kStreamRowsBytes;
+  p.vec_idx = vec_idx_for(topk_idx, num_tokens, topk);
   p.wide_idx = wide_idx_for(topk_idx, num_tokens, topk);
   return from_hip(launch_dispatch(p, dtype, stream));
 }
@@ -187,6 +196,7 @@ extern "C" int ll_moe_combine(void* layout, int max_tokens, int num_tokens, int 
   p.slices = shape.slices;
   p.tile = shape.tile;
   p.block = shape.block;
+  p.vec_idx = vec_idx_for(topk_idx, num_tokens, topk);
   return from_hip(launch_combine(p, stream));
 }
 

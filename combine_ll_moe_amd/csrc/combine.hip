@@ -28,7 +28,7 @@
 
 namespace llmoe {
 
-template <int MAXK, bool STREAM>
+template <int MAXK, bool STREAM, int VEC>
 __global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const CombineParams P) {
   __shared__ RouteShared rs;
   extern __shared__ int hist[];  // hist_cap_for(num_experts) ints
@@ -44,11 +44,13 @@ __global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const Combine
   const int t1 = t0 + P.tile < P.num_tokens ? t0 + P.tile : P.num_tokens;
 
   // the tile's slots in LDS (wavefront 0 ranks them; a barrier shares
-  // them). Every wavefront ranking its own copy instead, which saves that
-  // barrier, measured slower for large batches (1024 tokens of 7168
-  // columns: 30.1 against 29.7 us) and no faster for small ones.
-  route_tile(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens, rs, hist,
-             hist_cap_for(P.num_experts));
+  // them), the table read by two 16-byte loads per thread and round (8
+  // single-entry loads when it cannot be read 4 entries at a time). Every
+  // wavefront ranking its own copy instead, which saves that barrier,
+  // measured slower for large batches (1024 tokens of 7168 columns: 30.1
+  // against 29.7 us) and no faster for small ones.
+  route_tile<VEC, false, VEC == 4 ? 2 : 8>(P.idx, t0, t1, P.topk, P.num_experts, P.max_tokens,
+                                           rs, hist, hist_cap_for(P.num_experts));
 
   const int chunks = P.hidden / 8;
   const int c = sl * (int)blockDim.x + tid;
@@ -72,26 +74,34 @@ __global__ void __launch_bounds__(kCombineMaxBlock) combine_kernel(const Combine
   gather_tile<MAXK, STREAM>(reinterpret_cast<const g32x4*>(P.y), t1 - t0, c, chunks, tok, out);
 }
 
-template <bool STREAM>
+template <bool STREAM, int VEC>
 static void launch_k(const CombineParams& p, int blocks, hipStream_t stream) {
   const size_t lds = sizeof(int) * hist_cap_for(p.num_experts);
   if (p.topk <= 2)
-    combine_kernel<2, STREAM><<<blocks, p.block, lds, stream>>>(p);
+    combine_kernel<2, STREAM, VEC><<<blocks, p.block, lds, stream>>>(p);
   else if (p.topk <= 4)
-    combine_kernel<4, STREAM><<<blocks, p.block, lds, stream>>>(p);
+    combine_kernel<4, STREAM, VEC><<<blocks, p.block, lds, stream>>>(p);
   else if (p.topk <= 8)
-    combine_kernel<8, STREAM><<<blocks, p.block, lds, stream>>>(p);
+    combine_kernel<8, STREAM, VEC><<<blocks, p.block, lds, stream>>>(p);
   else
-    combine_kernel<16, STREAM><<<blocks, p.block, lds, stream>>>(p);
+    combine_kernel<16, STREAM, VEC><<<blocks, p.block, lds, stream>>>(p);
+}
+
+template <bool STREAM>
+static void launch_vec(const CombineParams& p, int blocks, hipStream_t stream) {
+  if (p.vec_idx)
+    launch_k<STREAM, 4>(p, blocks, stream);
+  else
+    launch_k<STREAM, 1>(p, blocks, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int tiles = p.num_tokens > 0 ? (p.num_tokens + p.tile - 1) / p.tile : 1;
   const int blocks = tiles * p.slices;
   if (p.stream_rows)
-    launch_k<true>(p, blocks, stream);
+    launch_vec<true>(p, blocks, stream);
   else
-    launch_k<false>(p, blocks, stream);
+    launch_vec<false>(p, blocks, stream);
   return hipGetLastError();
 }
 

@@ -532,7 +532,8 @@ __global__ void __launch_bounds__(BLOCK) dispatch_direct_kernel(const DispatchPa
       }
     }
   };
-  const int wslot = route_tile<VEC, true>(
+  // one 16-byte routing load per thread and round (single entries: 8)
+  const int wslot = route_tile<VEC, true, VEC == 4 ? 1 : 8>(
       P.idx, t0, t1, K, P.num_experts, P.max_tokens, rs, hist, hist_cap_for(P.num_experts),
       [&]() { load_row<kStage>(r, x + (size_t)t0 * units, units); },
       [&]() {
@@ -633,7 +634,7 @@ static hipError_t launch_lds(const DispatchParams& p, hipStream_t stream) {
 template <int DT>
 static hipError_t launch_modes(const DispatchParams& p, hipStream_t stream) {
   if (!p.line_align)
-    return p.wide_idx ? launch_direct<DT, 4>(p, stream) : launch_direct<DT, 1>(p, stream);
+    return p.vec_idx ? launch_direct<DT, 4>(p, stream) : launch_direct<DT, 1>(p, stream);
   return p.group_rows ? launch_lds<DT, true>(p, stream) : launch_lds<DT, false>(p, stream);
 }
 

@@ -25,7 +25,8 @@ struct DispatchParams {
   uint32_t msg_bytes;              // md
   uint32_t msg_stride;             // LDS path: bytes of one message buffer (one per tile token)
   int line_align;                  // 64 MiB of rows or more: the LDS path, whole-line stores
-  int wide_idx;                    // routing prologue reads 4 entries per load
+  int vec_idx;                     // routing table readable 4 entries per load (register path)
+  int wide_idx;                    // the same, and read so on the LDS path (large tables)
 };
 
 struct CombineParams {
@@ -43,6 +44,7 @@ struct CombineParams {
   int slices;                      // workgroups per tile, each a contiguous run of columns
   int block;                       // threads per workgroup (one 16-byte column chunk each)
   int stream_rows;                 // read the expert rows with non-temporal loads
+  int vec_idx;                     // routing table readable 4 entries per load
 };
 
 struct SendParams {                // two-phase combine, expert side

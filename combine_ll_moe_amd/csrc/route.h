@@ -19,11 +19,14 @@
 // count leaves LDS to other workgroups); more experts take more passes over
 // the earlier entries. Loads are unconditional (indices
 // clamped into the table, clamped lanes masked afterwards), so the compiler
-// issues them back to back. A round of loads covers 8 loads per thread of
-// VEC consecutive entries each: VEC = 4 (16-byte loads, for large tables
-// that are 16-byte aligned and a whole number of 4-entry vectors) covers
-// 8192 entries per round of a 256-thread workgroup, so a batch of 1024
-// tokens of 8 picks needs one load round trip instead of four.
+// issues them back to back. A round of loads covers UNROLL loads per thread
+// of VEC consecutive entries each (VEC = 4: 16-byte loads, for tables that
+// are 16-byte aligned and a whole number of 4-entry vectors). Fewer load
+// instructions per thread measured faster even where they take more
+// rounds: 1 load of 4 entries per thread and round in the register-path
+// dispatch, 2 in the combine; 8 loads of 4 entries in the dispatch of
+// 64 MiB or more, whose batch of 1024 tokens of 8 picks then takes one
+// round (each choice is measured where it is made).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -133,7 +136,7 @@ __device__ __forceinline__ void for_each_distinct(int value, const F& f) {
 // histogram pass covers the experts; rs.slot is still written (by
 // wavefront 0) and is visible after the caller's next barrier. Otherwise
 // the return value is meaningless and rs.slot is visible on return.
-template <int VEC = 1, bool WAVE_SLOTS = false, typename Issue = NoOverlap,
+template <int VEC = 1, bool WAVE_SLOTS = false, int UNROLL = 8, typename Issue = NoOverlap,
           typename Overlap = NoOverlap, typename Ready = NoOverlap>
 __device__ __forceinline__ int route_tile(const int32_t* __restrict__ idx, int t0, int t1,
                                            int topk, int num_experts, int max_tokens,
@@ -145,7 +148,7 @@ __device__ __forceinline__ int route_tile(const int32_t* __restrict__ idx, int t
   const int nthreads = blockDim.x;
   const int first = t0 * topk;         // entries before the tile: [0, first)
   const int n = (t1 - t0) * topk;      // the tile's entries: [first, first + n)
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = UNROLL;
   typedef typename IdxVec<VEC>::type Vec;
   const Vec* tab = reinterpret_cast<const Vec*>(idx);
   const int stride = nthreads * kUnroll * VEC;  // entries per round
