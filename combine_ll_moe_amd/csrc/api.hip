@@ -34,7 +34,9 @@ uint32_t dispatch_lds_budget(int num_experts) {
 // is 16-byte aligned and a whole number of 4-entry vectors (vec_idx), with
 // few loads per thread and round: one in the register-path dispatch (128
 // tokens of 7168 columns: 5.18 against 5.40 us with 8 single-entry loads;
-// 512 tokens of 4096 columns, three rounds: 11.60 against 11.95), two in
+// 512 tokens of 4096 columns, three rounds: 11.60 against 11.95; 2048
+// tokens of 1024 columns, sixteen rounds: 16.0 against 16.3 with 8 loads of
+// 4 entries), two in
 // the combine (128 tokens of 7168 columns, step 10.12 against 10.36 us with
 // both changes). The dispatch of 64 MiB or more reads 8 vectors per thread
 // and round, but only for tables of more than 4096 entries (wide_idx), so
