@@ -75,13 +75,15 @@ class Step:
                            w.dtype, q, xd, idd)
         oracle.dispatch(self.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, x, idx)
 
-    def combine(self, q, y: np.ndarray, idx: np.ndarray, wt: np.ndarray, y_dev=None):
+    def combine(self, q, y: np.ndarray, idx: np.ndarray, wt: np.ndarray, y_dev=None,
+                idx_dev=None):
         w = self.w
         n = idx.shape[0]
         yd = to_dev(y) if y_dev is None else y_dev
+        idd = to_dev(idx) if idx_dev is None else idx_dev
         out = torch.full((n, w.hidden), float("nan"), dtype=torch.float32, device=DEV)
         ll.ll_moe_combine(self.lay, w.capacity, n, w.hidden, w.num_experts, idx.shape[1],
-                          w.dtype, q, yd, to_dev(idx), to_dev(wt), out)
+                          w.dtype, q, yd, idd, to_dev(wt), out)
         ref = oracle.combine(self.img, w.capacity, w.hidden, w.num_experts, w.dtype, q, y, idx, wt)
         torch.cuda.synchronize()
         return out.cpu().numpy(), ref

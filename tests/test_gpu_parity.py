@@ -218,11 +218,15 @@ def test_largest_messages(shape):
     (1025, 5, 64, 0),    # 5125 entries, not a whole number of 4-entry loads
     (3000, 4, 64, 0),    # 12000 entries: two rounds of four-entry loads
     (1024, 8, 5000, 0),  # four-entry loads in both histogram passes (5000 experts)
+    (128, 8, 256, 0),    # 1024 entries, aligned: four per load on the register path
+    (128, 8, 256, 1),    # the same, misaligned: one per load
 ])
 def test_routing_table_load_widths(n, k, e, shift):
-    """The dispatch reads a long routing table four entries per load only
-    when it is 16-byte aligned and a multiple of 4 entries long; every case
-    must route exactly as the oracle does."""
+    """The dispatch and the combine read the routing table four entries per
+    load only when it is 16-byte aligned and a multiple of 4 entries long
+    (the dispatch of 64 MiB or more only when it is also longer than 4096
+    entries); every case must route exactly as the oracle does, through
+    both kernels, with the table at the same (mis)aligned address."""
     w = W.Workload("tab", n, 64, e, k, W.BF16, "hotset", seed=n + k + shift)
     x, idx, wt, y = _inputs(w)
     buf = torch.zeros(idx.size + 4, dtype=torch.int32, device=DEV)
@@ -234,8 +238,8 @@ def test_routing_table_load_widths(n, k, e, shift):
     for q in (0, 1):
         st.dispatch(q, x, idx, idx_dev=idx_dev)
         st.check_dispatch(q, idx)
-        out, ref = st.combine(q, y, idx, wt)
-        check_combine(out, ref)
+        out, ref = st.combine(q, y, idx, wt, idx_dev=idx_dev)
+        assert check_combine(out, ref) == 0, "combine outputs differ in bits"
 
 
 @pytest.mark.parametrize("shape", [
